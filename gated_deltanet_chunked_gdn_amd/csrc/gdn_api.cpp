@@ -1,0 +1,317 @@
+// C ABI of the GDN chunked prefill: argument validation, planning (chunks,
+// context-parallel segments), workspace carving and kernel dispatch.
+// Validation and planning are plain host code that runs before any HIP call,
+// so every error path is reachable without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void *ptr, size_t a) {
+  return ((uintptr_t)ptr % a) == 0;
+}
+
+// (K, V) pairs the kernels are compiled for.  fp32 tiles take twice the LDS,
+// so fp32 stops at 64.
+bool supported_kv(int dtype, int k, int v) {
+  if (dtype == GDN_BF16)
+    return (k == v && (k == 32 || k == 64 || k == 128)) || (k == 64 && v == 128) ||
+           (k == 128 && v == 64);
+  return (k == 32 || k == 64) && (v == 32 || v == 64);
+}
+
+// Validates the problem description; fills plan on success.
+int validate(const gdn_problem_t *p, gdn::Plan *plan) {
+  if (!p) return fail(GDN_ERR_INVALID_ARG, "problem descriptor is NULL");
+  if (p->B <= 0 || p->T < 0 || p->Hq <= 0 || p->Hv <= 0 || p->K <= 0 || p->V <= 0)
+    return fail(GDN_ERR_INVALID_ARG,
+                "dimensions must be positive (B=%d T=%d Hq=%d Hv=%d K=%d V=%d)",
+                p->B, p->T, p->Hq, p->Hv, p->K, p->V);
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", p->dtype);
+  if (p->Hv % p->Hq != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "Hv=%d is not a multiple of Hq=%d", p->Hv, p->Hq);
+  if (!supported_kv(p->dtype, p->K, p->V))
+    return fail(GDN_ERR_UNSUPPORTED,
+                "K=%d V=%d not supported for this dtype (bf16: K == V in {32, 64, "
+                "128}, (64, 128), (128, 64); fp32: K, V in {32, 64})",
+                p->K, p->V);
+  if (!(p->scale == p->scale)) return fail(GDN_ERR_INVALID_ARG, "scale is NaN");
+  gdn::Plan pl;
+  int64_t maxlen = 0;
+  if (p->cu_seqlens) {
+    if (!p->cu_seqlens_host)
+      return fail(GDN_ERR_INVALID_ARG,
+                  "cu_seqlens given without its host copy cu_seqlens_host");
+    if (p->B != 1)
+      return fail(GDN_ERR_INVALID_ARG, "B must be 1 with cu_seqlens (got %d)", p->B);
+    if (p->N <= 0) return fail(GDN_ERR_INVALID_ARG, "N must be positive (got %d)", p->N);
+    const int32_t *cu = p->cu_seqlens_host;
+    if (cu[0] != 0) return fail(GDN_ERR_INVALID_ARG, "cu_seqlens[0] = %d, must be 0", cu[0]);
+    for (int n = 0; n < p->N; ++n) {
+      if (cu[n + 1] < cu[n])
+        return fail(GDN_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", n,
+                    cu[n], cu[n + 1]);
+      const int64_t len = cu[n + 1] - cu[n];
+      maxlen = std::max(maxlen, len);
+      if (len == 0) pl.has_empty = true;
+      pl.total_chunks += (len + 63) / 64;
+    }
+    if (cu[p->N] != p->T)
+      return fail(GDN_ERR_INVALID_ARG, "cu_seqlens[N] = %d but T = %d", cu[p->N], p->T);
+    pl.N = p->N;
+  } else {
+    if (p->cu_seqlens_host)
+      return fail(GDN_ERR_INVALID_ARG, "cu_seqlens_host given without cu_seqlens");
+    if (p->N != p->B)
+      return fail(GDN_ERR_INVALID_ARG, "N must equal B without cu_seqlens (N=%d B=%d)",
+                  p->N, p->B);
+    pl.N = p->B;
+    maxlen = p->T;
+    pl.has_empty = p->T == 0;
+    pl.total_chunks = (int64_t)p->B * ((p->T + 63) / 64);
+  }
+  pl.total_tokens = (int64_t)p->B * p->T;
+  if ((int64_t)p->B * p->T * std::max(p->Hq, p->Hv) * std::max(p->K, p->V) >
+      ((int64_t)1 << 40))
+    return fail(GDN_ERR_UNSUPPORTED, "problem too large");
+  // context-parallel segment length (in chunks)
+  int cp = p->cp_mode;
+  if (cp == -1) {
+    const char *env = getenv("GDN_CP");
+    if (env && *env) cp = atoi(env);
+  }
+  if (cp < -1) return fail(GDN_ERR_INVALID_ARG, "cp_mode %d invalid (-1, 0 or n > 0)", cp);
+  const int64_t maxchunks = (maxlen + 63) / 64;
+  int64_t seg;
+  if (cp == 0) {
+    seg = std::max<int64_t>(maxchunks, 1);
+  } else if (cp > 0) {
+    seg = cp;
+  } else {
+    // automatic: about one segment per compute unit, at least 8 chunks long
+    const int64_t work = pl.total_chunks * p->Hv;
+    seg = std::max<int64_t>(8, (work + 255) / 256);
+    seg = std::min<int64_t>(seg, std::max<int64_t>(maxchunks, 1));
+  }
+  pl.seg_chunks = (int)std::min<int64_t>(seg, 1 << 30);
+  pl.total_segs = 0;
+  pl.max_segs_per_seq = 0;
+  auto add_seq = [&](int64_t len) {
+    const int64_t nc = (len + 63) / 64;
+    const int64_t ns = (nc + pl.seg_chunks - 1) / pl.seg_chunks;
+    pl.total_segs += ns;
+    pl.max_segs_per_seq = std::max<int>(pl.max_segs_per_seq, (int)ns);
+  };
+  if (p->cu_seqlens) {
+    for (int n = 0; n < p->N; ++n) add_seq(p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n]);
+  } else {
+    for (int n = 0; n < p->B; ++n) add_seq(p->T);
+  }
+  if (pl.total_segs * p->Hv >= ((int64_t)1 << 31) ||
+      pl.total_chunks * p->Hv >= ((int64_t)1 << 31))
+    return fail(GDN_ERR_UNSUPPORTED, "problem too large for the launch grid");
+  *plan = pl;
+  return GDN_OK;
+}
+
+gdn::FwdWorkspace fwd_layout(const gdn_problem_t *p, const gdn::Plan &pl, size_t base) {
+  gdn::FwdWorkspace w;
+  size_t off = base;
+  const size_t es = p->dtype == GDN_BF16 ? 2 : 4;
+  const size_t kv = (size_t)p->K * p->V * 4;
+  w.chunk_prefix = off;
+  off = align256(off + (size_t)(pl.N + 1) * 4);
+  w.seg_prefix = off;
+  off = align256(off + (size_t)(pl.N + 1) * 4);
+  w.tmat = off;
+  off = align256(off + (size_t)pl.total_chunks * p->Hv * 64 * 64 * es);
+  w.hseg = off;
+  off = align256(off + (size_t)pl.total_segs * p->Hv * kv);
+  w.eseg = off;
+  off = align256(off + (size_t)pl.total_segs * p->Hv * kv);
+  w.flags = off;
+  off = align256(off + (size_t)pl.total_segs * p->Hv * 4);
+  w.total = off;
+  return w;
+}
+
+gdn::BwdWorkspace bwd_layout(const gdn_problem_t *p, const gdn::Plan &pl) {
+  gdn::BwdWorkspace w;
+  w.fwd = fwd_layout(p, pl, 0);
+  size_t off = w.fwd.total;
+  const size_t kv = (size_t)p->K * p->V * 4;
+  w.hstates = off;
+  off = align256(off + (size_t)pl.total_chunks * p->Hv * kv);
+  w.dstates = off;
+  off = align256(off + (size_t)pl.total_chunks * p->Hv * kv);
+  w.dseg = off;
+  off = align256(off + (size_t)pl.total_segs * p->Hv * kv);
+  w.deseg = off;
+  off = align256(off + (size_t)pl.total_segs * p->Hv * kv);
+  w.dflags = off;
+  off = align256(off + (size_t)pl.total_segs * p->Hv * 4);
+  w.dqk = off;
+  off = align256(off + (size_t)pl.total_chunks * 64 * p->Hv * 2 * p->K * 4);
+  w.total = off;
+  return w;
+}
+
+gdn::Problem to_problem(const gdn_problem_t *p) {
+  gdn::Problem q;
+  q.B = p->B;
+  q.T = p->T;
+  q.Hq = p->Hq;
+  q.Hv = p->Hv;
+  q.K = p->K;
+  q.V = p->V;
+  q.N = p->cu_seqlens ? p->N : p->B;
+  q.dtype = p->dtype;
+  q.scale = p->scale;
+  q.cu = p->cu_seqlens;
+  return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_last_error(void) { return g_err.c_str(); }
+
+size_t gdn_chunk_fwd_workspace_size(const gdn_problem_t *p) {
+  gdn::Plan pl;
+  if (validate(p, &pl) != GDN_OK) return 0;
+  return fwd_layout(p, pl, 0).total;
+}
+
+size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p) {
+  gdn::Plan pl;
+  if (validate(p, &pl) != GDN_OK) return 0;
+  return bwd_layout(p, pl).total;
+}
+
+int64_t gdn_plan_segments(const gdn_problem_t *p) {
+  gdn::Plan pl;
+  if (validate(p, &pl) != GDN_OK) return 0;
+  return pl.total_segs;
+}
+
+int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
+                  const float *g, const void *beta, const float *h0, void *o, float *ht,
+                  float *g_cum, float *A, float *h, void *workspace, size_t ws_bytes,
+                  void *stream) {
+  g_err.clear();
+  gdn::Plan pl;
+  int rc = validate(p, &pl);
+  if (rc != GDN_OK) return rc;
+  if (pl.total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+    return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 4) ||
+      !aligned(g, 4) || !aligned(h0, 4) || !aligned(ht, 4) || !aligned(A, 4) ||
+      !aligned(h, 4) || !aligned(g_cum, 4))
+    return fail(GDN_ERR_LAYOUT, "q, k, v must be 16-byte aligned; fp32 buffers 4-byte");
+  const gdn::FwdWorkspace wl = fwd_layout(p, pl, 0);
+  if (!workspace || ws_bytes < wl.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  gdn::FwdArgs a;
+  a.p = to_problem(p);
+  a.plan = pl;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.h0 = h0;
+  a.o = o;
+  a.ht = ht;
+  a.g_cum = g_cum;
+  a.A = A;
+  a.h = h;
+  a.ws = static_cast<char *>(workspace);
+  a.wl = wl;
+  hipError_t e = gdn::launch_fwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(GDN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
+                  const float *g, const void *beta, const float *A, const float *h0,
+                  const void *do_, const float *dht, void *dq, void *dk, void *dv,
+                  void *dbeta, float *dg, float *dh0, void *workspace, size_t ws_bytes,
+                  void *stream) {
+  g_err.clear();
+  gdn::Plan pl;
+  int rc = validate(p, &pl);
+  if (rc != GDN_OK) return rc;
+  if (pl.total_tokens > 0 &&
+      (!q || !k || !v || !g || !beta || !do_ || !dq || !dk || !dv || !dbeta || !dg))
+    return fail(GDN_ERR_INVALID_ARG,
+                "q, k, v, g, beta, do, dq, dk, dv, dbeta and dg are required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(do_, 16) ||
+      !aligned(dq, 4) || !aligned(dk, 4) || !aligned(dv, 4) || !aligned(g, 4) ||
+      !aligned(A, 16) || !aligned(h0, 4) || !aligned(dht, 4) || !aligned(dh0, 4) ||
+      !aligned(dg, 4))
+    return fail(GDN_ERR_LAYOUT, "q, k, v, do, A must be 16-byte aligned; fp32 buffers 4-byte");
+  const gdn::BwdWorkspace wl = bwd_layout(p, pl);
+  if (!workspace || ws_bytes < wl.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  gdn::BwdArgs a;
+  a.p = to_problem(p);
+  a.plan = pl;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.dout = do_;
+  a.g = g;
+  a.A = A;
+  a.h0 = h0;
+  a.dht = dht;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dbeta = dbeta;
+  a.dg = dg;
+  a.dh0 = dh0;
+  a.ws = static_cast<char *>(workspace);
+  a.wl = wl;
+  hipError_t e = gdn::launch_bwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(GDN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+int gdn_selftest(void) {
+  g_err.clear();
+  int rc = gdn::run_selftest();
+  if (rc != 0) return fail(GDN_ERR_HIP, "MFMA self-test failed (code %d)", rc);
+  return GDN_OK;
+}
+
+}  // extern "C"

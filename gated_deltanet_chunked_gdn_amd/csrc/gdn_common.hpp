@@ -1,0 +1,131 @@
+// Device helpers shared by the GDN kernels (gfx950 / CDNA4).
+//
+// Matrix products use the 16x16 MFMA family with a 64-lane wavefront:
+//   bf16: v_mfma_f32_16x16x32_bf16  (8 bf16 of A and of B per lane)
+//   fp32: v_mfma_f32_16x16x4_f32    (1 fp32 of A and of B per lane)
+// Operand convention used everywhere here: for C = X * Y (M x N, contraction
+// index k), X is stored in LDS as X[m][k] and Y as Yt[n][k], both contiguous
+// along k.  Lane l supplies X[m0 + (l & 15)][k0 + EPL*(l >> 4) + e] and
+// Yt[n0 + (l & 15)][k0 + EPL*(l >> 4) + e] for e < EPL; since A and B use the
+// same (lane group, slot) -> k assignment, the instruction's internal k
+// order does not matter.  The accumulator element i of lane l is
+// C[m0 + 4*(l >> 4) + i][n0 + (l & 15)].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int N>
+using TileArr = f32x4[N];  // N accumulator tiles held by one lane
+
+constexpr int kChunk = 64;  // tokens per chunk
+constexpr int kWave = 64;   // lanes per wavefront
+
+template <typename E>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  static constexpr int KS = 32;  // contraction length of one instruction
+  static constexpr int EPL = 8;  // elements per lane per operand
+  typedef bf16x8 frag;
+  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // 16-byte aligned LDS or global read of 8 contiguous elements
+  __device__ static __forceinline__ frag ld(const bf16 *p) {
+    return *reinterpret_cast<const frag *>(p);
+  }
+  // 8 elements at stride `stride` (element units), each scaled by w[e]
+  __device__ static __forceinline__ frag ld_strided_scaled(const bf16 *p, int stride,
+                                                  const float *w) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)p[e * stride] * w[e]);
+    return f;
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int KS = 4;
+  static constexpr int EPL = 1;
+  typedef float frag;
+  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ frag ld(const float *p) { return *p; }
+  __device__ static __forceinline__ frag ld_strided_scaled(const float *p, int stride,
+                                                  const float *w) {
+    return p[0] * w[0];
+  }
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename E>
+__device__ __forceinline__ E from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Store 4 consecutive elements (8 bytes for bf16, 16 for fp32).
+__device__ __forceinline__ void st4(bf16 *p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  v[2] = (bf16)c;
+  v[3] = (bf16)d;
+  *reinterpret_cast<bf16x4 *>(p) = v;
+}
+__device__ __forceinline__ void st4(float *p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4 *>(p) = f32x4{a, b, c, d};
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Inclusive prefix sum across the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    float y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Locate sequence n with prefix[n] <= x < prefix[n+1] (prefix non-decreasing,
+// prefix[0] = 0, x < prefix[N]).  Skips empty sequences.
+__device__ __forceinline__ int find_seq(const int32_t *prefix, int N, int64_t x) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)prefix[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Map a linear workgroup id so that ids dispatched to the same XCD (the
+// hardware deals workgroups round-robin over the 8 XCDs) cover a contiguous
+// range of work items; neighbouring work items (e.g. the v-heads that share a
+// q/k head) then share one XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
+  constexpr int kXcd = 8;
+  if (nblocks % kXcd != 0) return bid;
+  const int64_t per = nblocks / kXcd;
+  return (bid % kXcd) * per + bid / kXcd;
+}
+
+}  // namespace gdn

@@ -1,0 +1,80 @@
+// Internal interface between the C ABI layer (gdn_api.cpp: validation,
+// planning, workspace carving) and the HIP kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace gdn {
+
+// Host-side plan of one problem.  Sequences are cut into 64-token chunks
+// (never crossing a sequence end) and the chunks of a sequence into
+// segments of `seg_chunks` chunks, the unit of intra-GPU context parallelism.
+struct Plan {
+  int N = 0;
+  int seg_chunks = 1;
+  int64_t total_chunks = 0;  // sum over sequences of ceil(len / 64)
+  int64_t total_segs = 0;    // sum over sequences of ceil(chunks / seg_chunks)
+  int max_segs_per_seq = 0;
+  bool has_empty = false;   // some sequence has no tokens
+  int64_t total_tokens = 0;
+};
+
+// Byte offsets of the pieces of a workspace (all 256-byte aligned).
+struct FwdWorkspace {
+  size_t chunk_prefix = 0;  // int32 [N+1]
+  size_t seg_prefix = 0;    // int32 [N+1]
+  size_t tmat = 0;          // element type [NC][Hv][64][64]: per-chunk T
+  size_t hseg = 0;          // fp32 [NS][Hv][K][V]: segment end states (pass 1)
+  size_t eseg = 0;          // fp32 [NS][Hv][K][V]: propagated starts (pass 2)
+  size_t flags = 0;         // int32 [NS][Hv]: eseg non-zero
+  size_t total = 0;
+};
+
+struct BwdWorkspace {
+  FwdWorkspace fwd;  // forward state recompute (its own pieces)
+  size_t hstates = 0;   // fp32 [NC][Hv][K][V]: state entering each chunk
+  size_t dstates = 0;   // fp32 [NC][Hv][K][V]: gradient w.r.t. state leaving each chunk
+  size_t dseg = 0;      // fp32 [NS][Hv][K][V]: reverse segment partials
+  size_t deseg = 0;     // fp32 [NS][Hv][K][V]
+  size_t dflags = 0;    // int32 [NS][Hv]
+  size_t dqk = 0;       // fp32 [NC*64][Hv][2][K]: per-v-head dq, dk before the group sum
+  size_t total = 0;
+};
+
+struct Problem {
+  int B, T, Hq, Hv, K, V, N;
+  int dtype;  // 0 fp32, 1 bf16
+  float scale;
+  const int32_t *cu;  // device, or null (uniform rows of T tokens)
+};
+
+struct FwdArgs {
+  Problem p;
+  Plan plan;
+  const void *q, *k, *v, *beta;
+  const float *g, *h0;
+  void *o;
+  float *ht, *g_cum, *A, *h;
+  char *ws;
+  FwdWorkspace wl;
+};
+
+struct BwdArgs {
+  Problem p;
+  Plan plan;
+  const void *q, *k, *v, *beta, *dout;
+  const float *g, *A, *h0, *dht;
+  void *dq, *dk, *dv, *dbeta;
+  float *dg, *dh0;
+  char *ws;
+  BwdWorkspace wl;
+};
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+int run_selftest();
+
+}  // namespace gdn

@@ -1,0 +1,129 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule chunked prefill.
+ *
+ * The operator is the GDN ("Gated Delta Rule") chunked prefill that the
+ * FlashQLA pages describe: the FlashQLA article's "高级 API 示例" section
+ * (chunk_gated_delta_rule(q, k, v, g, beta, scale, initial_state,
+ * output_final_state, cu_seqlens) -> (o, final_state)) and its "底层 API"
+ * section (chunk_gated_delta_rule_fwd -> (g, A, o, h, final_state) and
+ * chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht, scale,
+ * initial_state, cu_seqlens) -> (dq, dk, dv, db, dg, dh0)).  The pages print
+ * the signatures and the input shapes only.  The recurrence computed, per
+ * sequence n and v-head h, with the state S stored K x V (fp32):
+ *
+ *   S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = scale * S_t^T q_t
+ *
+ * with S_{-1} = initial_state[n, h] (or 0) and final_state[n, h] = the last
+ * S.  v-head h reads q/k head h / (Hv / Hq).
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   q, k        [B, T, Hq, K]      dtype of the problem (GDN_F32 or GDN_BF16)
+ *   v, o, do    [B, T, Hv, V]      problem dtype
+ *   beta        [B, T, Hv]         problem dtype
+ *   g           [B, T, Hv]         fp32, the raw log-gate (decay = exp(g))
+ *   initial_state, final_state, dht, dh0
+ *               [N, Hv, K, V]      fp32
+ *   g_cum       [B, T, Hv]         fp32, gate cumsum inside each 64-token chunk
+ *   A           [B, T, Hv, 64]     fp32, per chunk the unit-lower-triangular
+ *                                  T = (I + strict_lower(diag(beta) K K^T *
+ *                                  exp(gamma_r - gamma_j)))^-1; row r of a
+ *                                  chunk is stored at that row's token
+ *   h           [NC, Hv, K, V]     fp32, state entering each chunk; NC is the
+ *                                  total chunk count (sum over sequences of
+ *                                  ceil(len / 64)), chunks numbered in token
+ *                                  order
+ *   dq, dk      [B, T, Hq, K]      problem dtype (summed over each q/k group)
+ *   dv          [B, T, Hv, V], dbeta [B, T, Hv]: problem dtype; dg [B,T,Hv] fp32
+ * With cu_seqlens, B must be 1, T is the total packed length and sequence n
+ * covers tokens [cu[n], cu[n+1]); chunks never cross sequences.
+ *
+ * Ownership: every buffer belongs to the caller.  The library allocates no
+ * device memory; scratch comes from the caller's workspace (size from the
+ * *_workspace_size calls, 256-byte aligned).  It keeps no state between
+ * calls apart from the thread-local error message.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t, NULL = default
+ * stream) and the call returns without waiting for it.  No host
+ * synchronisation happens inside.
+ *
+ * Errors: a non-zero return means nothing was enqueued (validation errors)
+ * or a launch failed (GDN_ERR_HIP); gdn_last_error() then describes it.
+ * Nothing is thrown across this boundary.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+
+enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* null required pointer, bad dims, bad cu_seqlens */
+  GDN_ERR_UNSUPPORTED = 2, /* Hv % Hq != 0, K or V not in {32, 64, 128}, dtype */
+  GDN_ERR_LAYOUT = 3,      /* pointer not aligned to 16 bytes */
+  GDN_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned */
+  GDN_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+};
+
+typedef struct {
+  int32_t B, T, Hq, Hv, K, V; /* T = total packed tokens when cu_seqlens set */
+  int32_t N;                  /* sequences: B, or len(cu_seqlens) - 1 */
+  int32_t dtype;              /* gdn_dtype_t */
+  float scale;                /* output scale; callers usually pass K^-0.5 */
+  const int32_t *cu_seqlens;      /* device [N+1] or NULL */
+  const int32_t *cu_seqlens_host; /* host copy of the same; required iff
+                                     cu_seqlens != NULL (sizes the launch
+                                     without a device->host read) */
+  int32_t cp_mode; /* intra-GPU context parallelism: -1 automatic, 0 off,
+                      n > 0 = split sequences into segments of n chunks */
+} gdn_problem_t;
+
+/* Workspace bytes gdn_chunk_fwd / gdn_chunk_bwd need for this problem
+ * (0 if the problem is invalid; gdn_last_error() says why). */
+size_t gdn_chunk_fwd_workspace_size(const gdn_problem_t *p);
+size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p);
+
+/* Forward (chunk_gated_delta_rule_fwd of the FlashQLA article, "底层 API").
+ * Required: q k v g beta o.  Optional (NULL = not wanted / absent):
+ * h0 (initial state, else zero), ht (final state = output_final_state),
+ * g_cum, A, h (per-chunk entering states, the training-mode extras). */
+int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k,
+                  const void *v, const float *g, const void *beta,
+                  const float *h0, void *o, float *ht, float *g_cum, float *A,
+                  float *h, void *workspace, size_t ws_bytes, void *stream);
+
+/* Backward (chunk_gated_delta_rule_bwd of the same section).  g is the raw
+ * log-gate; dg is with respect to it.  A (as written by gdn_chunk_fwd) is
+ * optional: NULL recomputes it.  h0 and dht are optional (zero), dh0 is
+ * optional output.  Required: q k v g beta do dq dk dv dbeta dg. */
+int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k,
+                  const void *v, const float *g, const void *beta,
+                  const float *A, const float *h0, const void *do_,
+                  const float *dht, void *dq, void *dk, void *dv, void *dbeta,
+                  float *dg, float *dh0, void *workspace, size_t ws_bytes,
+                  void *stream);
+
+/* Number of context-parallel segments the forward would launch for this
+ * problem (host-only planning query; 0 if invalid). */
+int64_t gdn_plan_segments(const gdn_problem_t *p);
+
+/* Thread-local description of the last non-zero return ("" if none). */
+const char *gdn_last_error(void);
+
+/* Runs the library's MFMA lane-layout self-check on the current device:
+ * 0 when the bf16 and fp32 matrix instructions give the products the
+ * kernels assume, GDN_ERR_HIP otherwise (synchronous; diagnostics only). */
+int gdn_selftest(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,123 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad problems with the documented codes before
+any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_chunked_gdn_amd as gdn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = gdn.lib()
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def prob(**kw):
+    d = dict(B=1, T=256, Hq=2, Hv=4, K=128, V=128, N=1, dtype=gdn.GDN_BF16, scale=0.088,
+             cu_seqlens=None, cu_seqlens_host=None, cp_mode=-1)
+    d.update(kw)
+    return gdn.GdnProblem(**d)
+
+
+def ws(p):
+    return gdn.lib().gdn_chunk_fwd_workspace_size(ctypes.byref(p))
+
+
+def fwd_rc(p, ptr=16, wsb=1 << 30, workspace=1 << 20):
+    L = gdn.lib()
+    P = ctypes.c_void_p
+    return L.gdn_chunk_fwd(ctypes.byref(p), P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), None,
+                           P(ptr), None, None, None, None, P(workspace), wsb, None)
+
+
+def test_valid_problem_sizes():
+    p = prob()
+    assert ws(p) > 0
+    assert gdn.lib().gdn_chunk_bwd_workspace_size(ctypes.byref(p)) > ws(p)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(Hq=0), 1), (dict(K=-1), 1),
+    (dict(Hq=3, Hv=4), 2), (dict(K=96), 2), (dict(V=256), 2), (dict(dtype=7), 2),
+    (dict(dtype=gdn.GDN_F32, K=128, V=128), 2),
+    (dict(N=2), 1), (dict(cp_mode=-5), 1),
+])
+def test_invalid_problems(kw, code):
+    p = prob(**kw)
+    assert ws(p) == 0
+    assert fwd_rc(p) == code
+    assert gdn.last_error() != ""
+
+
+def test_cu_seqlens_validation():
+    import numpy as np
+    good = np.array([0, 10, 10, 256], dtype=np.int32)
+    host = good.ctypes.data_as(ctypes.c_void_p)
+    p = prob(N=3, cu_seqlens=16, cu_seqlens_host=host.value)
+    assert ws(p) > 0
+    assert gdn.lib().gdn_plan_segments(ctypes.byref(p)) >= 2
+    bad_cases = [np.array([1, 10, 20, 256], np.int32), np.array([0, 20, 10, 256], np.int32),
+                 np.array([0, 10, 20, 255], np.int32)]
+    for arr in bad_cases:
+        h = arr.ctypes.data_as(ctypes.c_void_p)
+        p = prob(N=3, cu_seqlens=16, cu_seqlens_host=h.value)
+        assert ws(p) == 0 and fwd_rc(p) == 1
+    # device pointer without host copy, B != 1, host copy without device pointer
+    assert fwd_rc(prob(N=3, cu_seqlens=16)) == 1
+    assert fwd_rc(prob(B=2, N=3, cu_seqlens=16, cu_seqlens_host=host.value)) == 1
+    assert fwd_rc(prob(cu_seqlens_host=host.value)) == 1
+
+
+def test_null_and_misaligned_pointers_and_workspace():
+    p = prob()
+    L = gdn.lib()
+    P = ctypes.c_void_p
+    rc = L.gdn_chunk_fwd(ctypes.byref(p), None, P(16), P(16), P(16), P(16), None, P(16),
+                         None, None, None, None, P(1 << 20), 1 << 30, None)
+    assert rc == 1
+    assert fwd_rc(p, ptr=18) == 3                 # q not 16-byte aligned
+    assert fwd_rc(p, wsb=16) == 4                  # workspace too small
+    assert fwd_rc(p, workspace=0) == 4             # no workspace
+    assert fwd_rc(p, workspace=(1 << 20) + 64) == 4  # workspace misaligned
+
+
+def test_bwd_validation():
+    p = prob(Hq=3)
+    L = gdn.lib()
+    P = ctypes.c_void_p
+    rc = L.gdn_chunk_bwd(ctypes.byref(p), *([P(16)] * 15), P(1 << 20), 1 << 30, None)
+    assert rc == 2
+    p = prob()
+    rc = L.gdn_chunk_bwd(ctypes.byref(p), P(16), P(16), P(16), P(16), P(16), None, None,
+                         P(16), None, None, P(16), P(16), P(16), P(16), None,
+                         P(1 << 20), 1 << 30, None)
+    assert rc == 1  # dq missing
+
+
+def test_plan_segments_cp_modes():
+    L = gdn.lib()
+    p = prob(T=8192, Hv=64, Hq=32)
+    assert L.gdn_plan_segments(ctypes.byref(prob(T=8192, Hv=64, Hq=32, cp_mode=0))) == 1
+    assert L.gdn_plan_segments(ctypes.byref(prob(T=8192, Hv=64, Hq=32, cp_mode=16))) == 8
+    auto = L.gdn_plan_segments(ctypes.byref(p))
+    assert 2 <= auto <= 16
+    assert L.gdn_plan_segments(ctypes.byref(prob(T=65536, Hv=8, Hq=4))) >= 16
+
+
+def test_empty_problem_is_valid():
+    p = prob(T=0)
+    assert ws(p) > 0

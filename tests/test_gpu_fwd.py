@@ -1,0 +1,171 @@
+"""GPU forward parity: the HIP path through the C ABI vs the fp64 oracle.
+
+Tolerance (relative Frobenius error over a whole output): 1e-5 for fp32
+inputs, 1e-2 for bf16 inputs.  Full-size workloads compare every output of a
+sample of (sequence, v-head) units that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.gpu_util import TOL, announce, oracle_fwd, rel, to_dev, token_mask
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_chunked_gdn_amd as g
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    g.lib()
+    return g
+
+
+def run_fwd(gdn, p, cp_mode=-1, want_inter=False):
+    d = to_dev(p)
+    out = gdn.chunk_gated_delta_rule_fwd(
+        d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
+        initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+        output_final_state=True, return_intermediates=want_inter, cp_mode=cp_mode)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_mfma_selftest(gdn):
+    announce("selftest")
+    gdn.selftest()
+
+
+def check(gdn, p, dtype, cp_mode=-1, label=""):
+    announce(f"fwd {label} cp={cp_mode}")
+    _, _, o, _, ht = run_fwd(gdn, p, cp_mode)
+    ro, rht = oracle_fwd(p)
+    eo, eh = rel(o, ro), rel(ht, rht)
+    assert eo <= TOL[dtype], f"o rel err {eo:.3e} ({label})"
+    assert eh <= TOL[dtype], f"final_state rel err {eh:.3e} ({label})"
+    return eo, eh
+
+
+def test_tiny_f32_workload(gdn):
+    p = synth.make(synth.WORKLOADS["tiny_f32"])
+    check(gdn, p, "f32", label="tiny_f32")
+
+
+@pytest.mark.parametrize("gate", ["default", "slow", "nodecay"])
+@pytest.mark.parametrize("cp", [0, 1, 2])
+def test_tiny_f32_gates_and_cp(gdn, gate, cp):
+    p = synth.make(synth.WORKLOADS["tiny_f32"], gate=gate, with_h0=True)
+    check(gdn, p, "f32", cp_mode=cp, label=f"tiny_f32 {gate}")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 257])
+@pytest.mark.parametrize("kv", [(128, 128), (64, 64), (64, 128), (128, 64), (32, 32)])
+def test_bf16_ragged_lengths(gdn, T, kv):
+    K, V = kv
+    p = synth.custom(2, T, 2, 4, K, V, dtype="bf16", seed=T, gate="slow", h0=True)
+    check(gdn, p, "bf16", cp_mode=1, label=f"T={T} K={K} V={V}")
+
+
+@pytest.mark.parametrize("kv", [(32, 32), (64, 64), (32, 64), (64, 32)])
+def test_f32_shapes(gdn, kv):
+    K, V = kv
+    p = synth.custom(1, 150, 1, 3, K, V, dtype="f32", seed=3, gate="slow", h0=True)
+    check(gdn, p, "f32", cp_mode=1, label=f"f32 K={K} V={V}")
+
+
+@pytest.mark.parametrize("gate", ["default", "slow", "nodecay"])
+def test_varlen_with_empty_and_short(gdn, gate):
+    lengths = [0, 1, 64, 130, 0, 700, 63, 129]
+    p = synth.custom(1, 0, 2, 4, 128, 128, dtype="bf16", seed=11, gate=gate,
+                     lengths=lengths, h0=True)
+    for cp in (0, 2, -1):
+        check(gdn, p, "bf16", cp_mode=cp, label=f"varlen {gate}")
+
+
+def test_gqa_grouping_matches_repeated_heads(gdn):
+    p = synth.custom(1, 300, 2, 6, 64, 64, dtype="bf16", seed=4, gate="slow", h0=True)
+    _, _, o1, _, h1 = run_fwd(gdn, p, cp_mode=2)
+    p2 = dict(p)
+    p2["q"] = p["q"].repeat_interleave(3, dim=2)
+    p2["k"] = p["k"].repeat_interleave(3, dim=2)
+    _, _, o2, _, h2 = run_fwd(gdn, p2, cp_mode=2)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_cp_split_agrees_with_unsplit_and_is_deterministic(gdn):
+    p = synth.custom(1, 4096, 2, 4, 128, 128, dtype="bf16", seed=8, gate="slow", h0=True)
+    _, _, o0, _, h0 = run_fwd(gdn, p, cp_mode=0)
+    for cp in (1, 3, 16):
+        _, _, o1, _, h1 = run_fwd(gdn, p, cp_mode=cp)
+        assert rel(o1, o0.double().cpu().numpy()) <= 1e-2
+        assert rel(h1, h0.double().cpu().numpy()) <= 1e-2
+    _, _, oa, _, ha = run_fwd(gdn, p, cp_mode=3)
+    _, _, ob, _, hb = run_fwd(gdn, p, cp_mode=3)
+    assert torch.equal(oa, ob) and torch.equal(ha, hb)
+
+
+def test_intermediates_gate_cumsum_and_inverse(gdn):
+    """g_cum and A against the oracle's chunked intermediates (fp64)."""
+    from oracle import chunked
+    p = synth.custom(1, 150, 1, 2, 64, 64, dtype="f32", seed=2, gate="default")
+    g_cum, A, o, h, ht = run_fwd(gdn, p, cp_mode=1, want_inter=True)
+    q, k, v, g, b = (p[n][0].double().numpy() for n in ("q", "k", "v", "g", "beta"))
+    for hh in range(2):
+        _, _, inter = chunked.chunk_forward_one(q[:, 0], k[:, 0], v[:, hh], g[:, hh],
+                                                b[:, hh], p["scale"],
+                                                np.zeros((64, 64)), 64)
+        for c, it in enumerate(inter):
+            s, n = 64 * c, len(it["gamma"])
+            assert rel(g_cum[0, s:s + n, hh], it["gamma"]) < 1e-5
+            assert rel(A[0, s:s + n, hh, :n], it["T"]) < 1e-5
+            assert rel(h[c, hh], it["S_in"]) < 1e-5 or np.abs(it["S_in"]).max() == 0
+
+
+# ------------------------------------------------------ full-size workloads
+
+def _sampled(gdn, name, heads, gate="default", T=None, cp=-1):
+    w = synth.WORKLOADS[name]
+    p = synth.make(w, gate=gate, T=T)
+    N = len(p["lengths"]) if "lengths" in p else w.B
+    mask = np.zeros((N, w.Hv), dtype=bool)
+    mask[:, heads] = True
+    announce(f"full {name} gate={gate} T={T} cp={cp}")
+    _, _, o, _, ht = run_fwd(gdn, p, cp_mode=cp)
+    ro, rht = oracle_fwd(p, unit_mask=mask)
+    tm = token_mask(p, mask)
+    o_np = o.double().cpu().numpy()
+    eo = rel(o_np[tm], ro[tm])
+    eh = rel(ht.double().cpu().numpy()[mask], rht[mask])
+    assert eo <= TOL[w.dtype], f"{name} o rel err {eo:.3e}"
+    assert eh <= TOL[w.dtype], f"{name} final rel err {eh:.3e}"
+    assert np.isfinite(o_np).all()
+
+
+def test_full_hv64_t8192(gdn):
+    _sampled(gdn, "hv64_t8192", heads=[0, 1, 17, 40, 63])
+
+
+def test_full_hv64_t8192_slow_decay(gdn):
+    _sampled(gdn, "hv64_t8192", heads=[0, 1, 33, 62], gate="slow")
+
+
+def test_full_hv8_t65536(gdn):
+    _sampled(gdn, "hv8_t65536", heads=[0, 5])
+
+
+def test_hv8_long_slow_decay_cp_fixup(gdn):
+    # slow decay: the segment fix-ups run over whole segments
+    _sampled(gdn, "hv8_t65536", heads=[3], gate="slow", T=16384)
+
+
+def test_hv8_long_no_decay(gdn):
+    _sampled(gdn, "hv8_t65536", heads=[2], gate="nodecay", T=8192)
+
+
+def test_full_varlen16_hv32(gdn):
+    _sampled(gdn, "varlen16_hv32", heads=[0, 31])
+
+
+def test_full_varlen16_hv32_slow(gdn):
+    _sampled(gdn, "varlen16_hv32", heads=[7], gate="slow")
