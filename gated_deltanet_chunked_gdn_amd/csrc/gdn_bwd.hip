@@ -1,9 +1,996 @@
-// Backward kernels of the GDN chunked prefill (gfx950).
-#include "gdn_common.hpp"
-#include "gdn_internal.h"
+// Backward kernels of the GDN chunked prefill for gfx950.
+//
+// The backward of the FlashQLA article's low-level API ("底层 API":
+// chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht, scale,
+// initial_state, cu_seqlens) -> dq, dk, dv, db, dg, dh0) is the reverse mode
+// of the chunked forward (see gdn_fwd.hip).  Per chunk, with S the entering
+// state, D = dL/dS' the gradient of the leaving state, and the forward
+// quantities recomputed (P = lower_incl(Q K^T * E), R, Vn = T R):
+//   dVn = scale P^T dO + diag(exp(gamma_L - gamma)) K D
+//   dR  = T^T dVn,      dA = -strict_lower(dR Vn^T)   (= -T^T dT T^T, dT = dVn R^T)
+//   dP  = scale lower_incl(dO Vn^T)
+//   dS  = exp(gamma_L) D + Q^T diag(scale e^gamma) dO - K^T diag(beta e^gamma) dR
+//   dq  = diag(scale e^gamma) dO S^T + (dP * E) K
+//   dk  = (dP * E)^T Q + (dKK + dKK^T) K - diag(beta e^gamma) dR S^T
+//         + diag(exp(gamma_L - gamma)) Vn D^T,          dKK = diag(beta) dA * E
+//   dv  = diag(beta) dR
+//   dbeta, dgamma from the rows and columns of these products; dg is the
+//   reverse cumulative sum of dgamma inside the chunk.
+// Kernels: (1) forward state recompute (the forward segment kernels, states
+// only), (2) the reverse recurrence for D, context-parallel with the same
+// exact fix-up scheme mirrored (segments run from a zero leaving gradient,
+// then the true one is propagated backwards with the homogeneous recurrence
+// until it is exactly zero), (3) a chunk-parallel kernel for the local
+// gradients, one workgroup per (chunk, q/k head) summing its v-heads' dq and
+// dk in a fixed order (no atomics).
+#include "gdn_seg.hpp"
 
 namespace gdn {
 
-hipError_t launch_bwd(const BwdArgs &, hipStream_t) { return hipErrorNotSupported; }
+enum { kRMain = 0, kRFix = 1 };
+
+// ------------------------------------------------- reverse recurrence for D
+template <typename E, int K, int V>
+struct RevLds {
+  using G = Geo<E, K, V>;
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + 64 * G::LDK;
+  static constexpr int oDOt = oK + 64 * G::LDK;   // dO^T [V][64]
+  static constexpr int oDt = oDOt + V * G::LDC;   // D^T  [V][K]
+  static constexpr int oTt = oDt + V * G::LDK;    // T^T  [64][64]
+  static constexpr int oPt = oTt + 64 * G::LDC;   // P^T  [64][64]
+  static constexpr int oDVnt = oPt + 64 * G::LDC; // dVn^T [V][64]
+  static constexpr int oXt = oDVnt + V * G::LDC;  // (-beta e^gamma T^T dVn)^T [V][64]
+  static constexpr int nE = oXt + V * G::LDC;
+  static constexpr int bytes = nE * (int)sizeof(E);
+};
+
+struct RSmem {
+  char *base;
+  GateLds gate;
+  float *wq;  // scale * exp(gamma)
+  float *wk;  // -beta * exp(gamma)
+  int *flag;
+};
+
+template <typename E, int K, int V, bool MAIN>
+__device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem &S, float scale) {
+  using G = Geo<E, K, V>;
+  using L = RevLds<E, K, V>;
+  E *sm = reinterpret_cast<E *>(S.base);
+  const int tid = threadIdx.x;
+  constexpr int PK = K / G::VEC, PVr = V / G::VEC, PTr = 64 / G::VEC;
+#pragma unroll
+  for (int m = 0; m < G::NQ; ++m) {
+    const int idx = tid + kThreads * m;
+    if (idx < G::PQ) {
+      const int r = idx / PK, cv = idx % PK;
+      *reinterpret_cast<uint4 *>(sm + L::oQ + r * G::LDK + cv * G::VEC) = pf.q[m];
+      *reinterpret_cast<uint4 *>(sm + L::oK + r * G::LDK + cv * G::VEC) = pf.k[m];
+    }
+  }
+  if (MAIN) {
+#pragma unroll
+    for (int m = 0; m < G::NV; ++m) {
+      const int idx = tid + kThreads * m;
+      if (idx < G::PV) {
+        const int r = idx / PVr, cv = idx % PVr;
+        const E *e8 = reinterpret_cast<const E *>(&pf.v[m]);
+#pragma unroll
+        for (int e = 0; e < G::VEC; ++e) sm[L::oDOt + (cv * G::VEC + e) * G::LDC + r] = e8[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < G::NTM; ++m) {
+    const int idx = tid + kThreads * m;
+    if (idx < G::PT) {
+      const int r = idx / PTr, cv = idx % PTr;
+      const E *e8 = reinterpret_cast<const E *>(&pf.t[m]);
+#pragma unroll
+      for (int e = 0; e < G::VEC; ++e) sm[L::oTt + (cv * G::VEC + e) * G::LDC + r] = e8[e];
+    }
+  }
+  if (tid < 64) {
+    const float gam = wave_incl_scan(pf.g);
+    const float gL = __shfl(gam, 63, 64);
+    const float eg = expf(gam);
+    S.gate.gam[tid] = gam;
+    S.gate.eg[tid] = eg;
+    S.gate.dec[tid] = expf(gL - gam);
+    S.gate.bet[tid] = pf.b;
+    S.wq[tid] = scale * eg;
+    S.wk[tid] = -pf.b * eg;
+  }
+}
+
+// Runs chunks c_end-1 down to c_begin of one (sequence, v-head), starting
+// from the leaving-state gradient in `st`.  kRMain: full reverse step.
+// kRFix: homogeneous reverse step (no dO), stops once the gradient is exactly
+// zero.  The gradient leaving every visited chunk is stored (kRMain) or
+// accumulated (kRFix) into dstates.
+template <typename E, int K, int V, int MODE>
+__device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
+                                        Tiles<Geo<E, K, V>::NTS> &st, const SeqInfo &si,
+                                        int64_t chunk_gid0, int c_begin, int c_end, int h) {
+  using G = Geo<E, K, V>;
+  using L = RevLds<E, K, V>;
+  using M = Mma<E>;
+  constexpr int KS = M::KS, EPL = M::EPL;
+  constexpr int NKK = K / KS;
+  constexpr int NKC = 64 / KS;
+  constexpr int NCH = G::NCH;
+  constexpr bool MAIN = MODE == kRMain;
+  const Problem &p = a.p;
+  E *sm = reinterpret_cast<E *>(S.base);
+  const E *sQ = sm + L::oQ;
+  const E *sK = sm + L::oK;
+  const E *sDOt = sm + L::oDOt;
+  E *sDt = sm + L::oDt;
+  const E *sTt = sm + L::oTt;
+  E *sPt = sm + L::oPt;
+  E *sDVnt = sm + L::oDVnt;
+  E *sXt = sm + L::oXt;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int rt = w & 3;
+  const int ct0 = (w >> 2) * NCH;
+  const float scale = p.scale;
+  const E *qp = reinterpret_cast<const E *>(a.q);
+  const E *kp = reinterpret_cast<const E *>(a.k);
+  const E *dop = reinterpret_cast<const E *>(a.dout);
+  const E *bp = reinterpret_cast<const E *>(a.beta);
+  const E *tmat = reinterpret_cast<const E *>(a.ws + a.wl.fwd.tmat);
+  float *dstates = reinterpret_cast<float *>(a.ws + a.wl.dstates);
+
+  if (c_begin >= c_end)
+    return MODE == kRFix ? !block_any(tiles_nonzero<E, K, V>(st), S.flag) : false;
+  Pref<E, K, V> pf;
+  {
+    const int c = c_end - 1;
+    pref_load<E, K, V, MAIN>(pf, p, qp, kp, dop, tmat, a.g, bp, si.tok0 + (int64_t)c * kChunk,
+                             min(kChunk, si.len - c * kChunk), h, chunk_gid0 + c);
+    rev_commit<E, K, V, MAIN>(pf, S, scale);
+    tiles_to_lds_t<E, K, V>(st, sDt);
+  }
+  __syncthreads();
+  bool zero_exit = false;
+  for (int c = c_end - 1; c >= c_begin && !zero_exit; --c) {
+    {
+      float *ds = dstates + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
+      tiles_store<E, K, V>(st, ds, nullptr, MODE == kRFix);
+    }
+    // ---- phase A: K D (rows of tile rt, half of V); P^T
+    typename M::frag ka[NKK];
+#pragma unroll
+    for (int ks = 0; ks < NKK; ++ks)
+      ka[ks] = M::ld(sK + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
+    f32x4 kd[NCH];
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) kd[c2] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKK; ++ks)
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2)
+        kd[c2] = M::mma(ka[ks],
+                        M::ld(sDt + (16 * (ct0 + c2) + lr) * G::LDK + ks * KS + EPL * lg),
+                        kd[c2]);
+    if (MAIN) {
+      const int pc0 = 2 * (w >> 2);
+      f32x4 qk[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < NKK; ++ks) {
+        const auto qa = M::ld(sQ + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+          if (pc0 + cc <= rt)
+            qk[cc] = M::mma(
+                qa, M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg), qk[cc]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int t = 16 * (pc0 + cc) + lr;
+        const float gt = S.gate.gam[t];
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * rt + 4 * lg + i;
+          pv[i] = (t <= s) ? qk[cc][i] * expf(S.gate.gam[s] - gt) : 0.f;
+        }
+        st4(sPt + t * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
+      }
+    }
+    __syncthreads();
+    if (c - 1 >= c_begin) {
+      const int c1 = c - 1;
+      pref_load<E, K, V, MAIN>(pf, p, qp, kp, dop, tmat, a.g, bp,
+                               si.tok0 + (int64_t)c1 * kChunk,
+                               min(kChunk, si.len - c1 * kChunk), h, chunk_gid0 + c1);
+    }
+    // ---- phase B: dVn = dec * (K D) + scale P^T dO
+    {
+      float dec_r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dec_r[i] = S.gate.dec[16 * rt + 4 * lg + i];
+      f32x4 x[NCH];
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2) x[c2] = zero4();
+      if (MAIN) {
+        typename M::frag pa[NKC];
+#pragma unroll
+        for (int ks = 0; ks < NKC; ++ks)
+          pa[ks] = M::ld(sPt + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+#pragma unroll
+        for (int ks = 0; ks < NKC; ++ks)
+#pragma unroll
+          for (int c2 = 0; c2 < NCH; ++c2)
+            x[c2] = M::mma(
+                pa[ks], M::ld(sDOt + (16 * (ct0 + c2) + lr) * G::LDC + ks * KS + EPL * lg),
+                x[c2]);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = dec_r[i] * kd[c2][i] + scale * x[c2][i];
+        st4(sDVnt + (16 * (ct0 + c2) + lr) * G::LDC + 16 * rt + 4 * lg, y[0], y[1], y[2], y[3]);
+      }
+    }
+    __syncthreads();
+    // ---- phase C: X = T^T dVn, scaled by -beta e^gamma
+    {
+      typename M::frag ta[NKC];
+#pragma unroll
+      for (int ks = 0; ks < NKC; ++ks)
+        ta[ks] = M::ld(sTt + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+      f32x4 x[NCH];
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2) x[c2] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKC; ++ks)
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2)
+          x[c2] = M::mma(
+              ta[ks], M::ld(sDVnt + (16 * (ct0 + c2) + lr) * G::LDC + ks * KS + EPL * lg),
+              x[c2]);
+      float wk_r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wk_r[i] = S.wk[16 * rt + 4 * lg + i];
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2)
+        st4(sXt + (16 * (ct0 + c2) + lr) * G::LDC + 16 * rt + 4 * lg, wk_r[0] * x[c2][0],
+            wk_r[1] * x[c2][1], wk_r[2] * x[c2][2], wk_r[3] * x[c2][3]);
+    }
+    __syncthreads();
+    // ---- phase D: D <- exp(gamma_L) D + Q^T diag(scale e^g) dO + K^T Xs
+    if (G::owns(w)) {
+      const float egL = S.gate.eg[63];
+      const int srt = G::srt(w), sct = G::sct(w);
+#pragma unroll
+      for (int m = 0; m < G::NTS; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[m][i] *= egL;
+#pragma unroll
+      for (int ks = 0; ks < NKC; ++ks) {
+        const int t0 = ks * KS + EPL * lg;
+        const auto kt = M::ld_strided(sK + t0 * G::LDK + 16 * srt + lr, G::LDK);
+#pragma unroll
+        for (int m = 0; m < G::NTS; ++m)
+          st[m] = M::mma(kt, M::ld(sXt + (16 * (sct + m) + lr) * G::LDC + ks * KS + EPL * lg),
+                         st[m]);
+        if (MAIN) {
+          const auto qt = M::ld_strided_scaled(sQ + t0 * G::LDK + 16 * srt + lr, G::LDK, S.wq + t0);
+#pragma unroll
+          for (int m = 0; m < G::NTS; ++m)
+            st[m] = M::mma(qt,
+                           M::ld(sDOt + (16 * (sct + m) + lr) * G::LDC + ks * KS + EPL * lg),
+                           st[m]);
+        }
+      }
+    }
+    tiles_to_lds_t<E, K, V>(st, sDt);
+    if (MODE == kRFix) {
+      zero_exit = !block_any(tiles_nonzero<E, K, V>(st), S.flag);
+    } else {
+      __syncthreads();
+    }
+    if (c - 1 >= c_begin && !zero_exit) {
+      rev_commit<E, K, V, MAIN>(pf, S, scale);
+      __syncthreads();
+    }
+  }
+  return zero_exit;
+}
+
+#define GDN_REV_LDS(E, K, V)                                                   \
+  __shared__ __attribute__((aligned(16))) char smem_[RevLds<E, K, V>::bytes]; \
+  __shared__ float sg_[6][64];                                                 \
+  __shared__ int sflag_[kNW];                                                  \
+  RSmem S;                                                                     \
+  S.base = smem_;                                                              \
+  S.gate.gam = sg_[0];                                                         \
+  S.gate.eg = sg_[1];                                                          \
+  S.gate.dec = sg_[2];                                                         \
+  S.gate.bet = sg_[3];                                                         \
+  S.wq = sg_[4];                                                               \
+  S.wk = sg_[5];                                                               \
+  S.flag = sflag_;
+
+template <typename E, int K, int V, int MODE>
+__global__ __launch_bounds__(kThreads) void rev_segment_kernel(BwdArgs a) {
+  using G = Geo<E, K, V>;
+  GDN_REV_LDS(E, K, V)
+  const Problem &p = a.p;
+  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = (int)(wid % p.Hv);
+  const int64_t sg = wid / p.Hv;
+  const SegLoc sl =
+      locate_segment(p, a.plan.seg_chunks,
+                     reinterpret_cast<const int32_t *>(a.ws + a.wl.fwd.chunk_prefix),
+                     reinterpret_cast<const int32_t *>(a.ws + a.wl.fwd.seg_prefix), sg);
+  if (MODE == kRFix && sl.j == sl.nseg - 1) return;
+  const int64_t KV = (int64_t)K * V;
+  float *dseg = reinterpret_cast<float *>(a.ws + a.wl.dseg);
+  float *deseg = reinterpret_cast<float *>(a.ws + a.wl.deseg);
+  int32_t *dflags = reinterpret_cast<int32_t *>(a.ws + a.wl.dflags);
+  Tiles<G::NTS> st;
+  if (MODE == kRMain) {
+    const float *src = (sl.j == sl.nseg - 1 && a.dht)
+                           ? a.dht + ((int64_t)sl.n * p.Hv + h) * KV : nullptr;
+    tiles_load<E, K, V>(st, src);
+  } else {
+    tiles_load<E, K, V>(st, dseg + ((sg + 1) * p.Hv + h) * KV);
+  }
+  const bool zero =
+      rev_run<E, K, V, MODE>(a, S, st, sl.si, sl.chunk0, sl.c_begin, sl.c_end, h);
+  if (MODE == kRMain) {
+    if (sl.nseg > 1) tiles_store<E, K, V>(st, dseg + (sg * p.Hv + h) * KV, nullptr, false);
+    if (sl.nseg == 1 && a.dh0)
+      tiles_store<E, K, V>(st, a.dh0 + ((int64_t)sl.n * p.Hv + h) * KV, nullptr, false);
+  } else {
+    if (!zero) tiles_store<E, K, V>(st, deseg + (sg * p.Hv + h) * KV, nullptr, false);
+    if (threadIdx.x == 0) dflags[sg * p.Hv + h] = zero ? 0 : 1;
+  }
+}
+
+template <typename E, int K, int V>
+__global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
+  using G = Geo<E, K, V>;
+  GDN_REV_LDS(E, K, V)
+  const Problem &p = a.p;
+  const int h = (int)(blockIdx.x % p.Hv);
+  const int n = (int)(blockIdx.x / p.Hv);
+  const SegLoc sl =
+      locate_sequence(p, a.plan.seg_chunks,
+                      reinterpret_cast<const int32_t *>(a.ws + a.wl.fwd.chunk_prefix),
+                      reinterpret_cast<const int32_t *>(a.ws + a.wl.fwd.seg_prefix), n);
+  const int64_t KV = (int64_t)K * V;
+  if (sl.nseg == 0) {  // empty sequence: dh0 = dht
+    if (a.dh0) {
+      float *dst = a.dh0 + ((int64_t)n * p.Hv + h) * KV;
+      const float *src = a.dht ? a.dht + ((int64_t)n * p.Hv + h) * KV : nullptr;
+      for (int64_t i = threadIdx.x; i < KV; i += blockDim.x) dst[i] = src ? src[i] : 0.f;
+    }
+    return;
+  }
+  if (sl.nseg == 1) return;
+  const float *dseg = reinterpret_cast<const float *>(a.ws + a.wl.dseg);
+  const float *deseg = reinterpret_cast<const float *>(a.ws + a.wl.deseg);
+  const int32_t *dflags = reinterpret_cast<const int32_t *>(a.ws + a.wl.dflags);
+  bool any_flag = false;
+  for (int j = (int)threadIdx.x; j < sl.nseg - 1; j += blockDim.x)
+    any_flag |= dflags[(sl.seg0 + j) * p.Hv + h] != 0;
+  if (!block_any(any_flag, S.flag)) {
+    if (a.dh0) {
+      float *dst = a.dh0 + ((int64_t)n * p.Hv + h) * KV;
+      const float *src = dseg + (sl.seg0 * p.Hv + h) * KV;
+      for (int64_t i = threadIdx.x; i < KV; i += blockDim.x) dst[i] = src[i];
+    }
+    return;
+  }
+  Tiles<G::NTS> st;
+  tiles_zero<E, K, V>(st);
+  bool nonzero = false;
+  for (int j = sl.nseg - 2; j >= 0; --j) {
+    const int64_t sg = sl.seg0 + j;
+    if (nonzero) {
+      const int c_begin = j * a.plan.seg_chunks;
+      const int c_end = min(c_begin + a.plan.seg_chunks, sl.si.nchunks);
+      rev_run<E, K, V, kRFix>(a, S, st, sl.si, sl.chunk0, c_begin, c_end, h);
+      __syncthreads();
+    }
+    if (dflags[sg * p.Hv + h]) {
+      Tiles<G::NTS> e;
+      tiles_load<E, K, V>(e, deseg + (sg * p.Hv + h) * KV);
+#pragma unroll
+      for (int m = 0; m < G::NTS; ++m) st[m] += e[m];
+    }
+    nonzero = block_any(tiles_nonzero<E, K, V>(st), S.flag);
+  }
+  if (a.dh0)
+    tiles_store<E, K, V>(st, a.dh0 + ((int64_t)n * p.Hv + h) * KV,
+                         dseg + (sl.seg0 * p.Hv + h) * KV, false);
+}
+
+// --------------------------------------------------------- local gradients
+template <typename E, int K, int V>
+struct LocCfg {
+  using G = Geo<E, K, V>;
+  static constexpr int VB = (sizeof(E) == 4) ? (V < 32 ? V : 32) : (V < 64 ? V : 64);
+  static constexpr int NVB = V / VB;
+  static constexpr int LDB = VB + G::PAD;
+  static constexpr int NCHB = VB / 32;  // V-block column tiles per half
+  static constexpr int NCHK = K / 32;   // key column tiles per half
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + 64 * G::LDK;
+  static constexpr int oT = oK + 64 * G::LDK;
+  static constexpr int oPt = oT + 64 * G::LDC;
+  static constexpr int oS = oPt + 64 * G::LDC;     // S block [K][LDB]
+  static constexpr int oD = oS + K * LDB;          // D block [K][LDB]; later dR [64][LDB]
+  static constexpr int oDO = oD + (K > 64 ? K : 64) * LDB;  // dO block [64][LDB]
+  static constexpr int oRt = oDO + 64 * LDB;       // R^T [VB][LDC]; later dVn^T
+  static constexpr int oVn = oRt + VB * G::LDC;    // Vn [64][LDB]
+  static constexpr int oPE = oVn + 64 * LDB;       // dP * E [64][LDC]
+  static constexpr int oKK = oPE + 64 * G::LDC;    // dKK [64][LDC]
+  static constexpr int nE = oKK + 64 * G::LDC;
+  static constexpr int bytes = nE * (int)sizeof(E);
+};
+
+// 16-lane (same lane group) sum over the 16 column lanes
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+
+template <typename E, int K, int V>
+__global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
+  using G = Geo<E, K, V>;
+  using C = LocCfg<E, K, V>;
+  using M = Mma<E>;
+  constexpr int KS = M::KS, EPL = M::EPL;
+  constexpr int NKK = K / KS;
+  constexpr int NKC = 64 / KS;
+  constexpr int NKB = C::VB / KS;
+  constexpr int VB = C::VB, LDB = C::LDB, NCHB = C::NCHB, NCHK = C::NCHK;
+  __shared__ __attribute__((aligned(16))) char smem_[C::bytes];
+  __shared__ float sgam[64], seg[64], sdec[64], sbet[64];
+  __shared__ float rowp[3][2][64];  // [de, db, rs/c][half][row]
+  __shared__ float colp[4][64];     // [row tile][col]
+  __shared__ float cpart[2][64];
+  __shared__ float glp[kNW];
+  E *sm = reinterpret_cast<E *>(smem_);
+  E *sQ = sm + C::oQ;
+  E *sK = sm + C::oK;
+  E *sT = sm + C::oT;
+  E *sPt = sm + C::oPt;
+  E *sS = sm + C::oS;
+  E *sD = sm + C::oD;
+  E *sDR = sm + C::oD;  // dR reuses the D block after its last use
+  E *sDO = sm + C::oDO;
+  E *sRt = sm + C::oRt;
+  E *sDVnt = sm + C::oRt;
+  E *sVn = sm + C::oVn;
+  E *sPE = sm + C::oPE;
+  E *sKK = sm + C::oKK;
+
+  const Problem &p = a.p;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int rt = w & 3, ch = w >> 2;
+  const int pc0 = 2 * ch;
+  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int hq = (int)(wid % p.Hq);
+  const int64_t gid = wid / p.Hq;
+  const int Gq = p.Hv / p.Hq;
+  const ChunkLoc cl =
+      locate_chunk(p, reinterpret_cast<const int32_t *>(a.ws + a.wl.fwd.chunk_prefix), gid);
+  const int64_t tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
+  const int rows = min(kChunk, cl.si.len - cl.c * kChunk);
+  const float scale = p.scale;
+  const E *qp = reinterpret_cast<const E *>(a.q);
+  const E *kp = reinterpret_cast<const E *>(a.k);
+  const E *vp = reinterpret_cast<const E *>(a.v);
+  const E *dop = reinterpret_cast<const E *>(a.dout);
+  const E *bp = reinterpret_cast<const E *>(a.beta);
+  const E *tmat = reinterpret_cast<const E *>(a.ws + a.wl.fwd.tmat);
+  const float *hst = reinterpret_cast<const float *>(a.ws + a.wl.hstates);
+  const float *dst = reinterpret_cast<const float *>(a.ws + a.wl.dstates);
+  E *dqp = reinterpret_cast<E *>(a.dq);
+  E *dkp = reinterpret_cast<E *>(a.dk);
+  E *dvp = reinterpret_cast<E *>(a.dv);
+  E *dbp = reinterpret_cast<E *>(a.dbeta);
+
+  // ---- chunk tiles of q and k (shared by the group's v-heads)
+  {
+    constexpr int VEC = G::VEC, PK = K / VEC;
+    for (int idx = tid; idx < 64 * PK; idx += kThreads) {
+      const int r = idx / PK, cv = idx % PK;
+      uint4 zq = make_uint4(0u, 0u, 0u, 0u), zk = zq;
+      if (r < rows) {
+        const int64_t off = ((tok0 + r) * p.Hq + hq) * K + cv * VEC;
+        zq = *reinterpret_cast<const uint4 *>(qp + off);
+        zk = *reinterpret_cast<const uint4 *>(kp + off);
+      }
+      *reinterpret_cast<uint4 *>(sQ + r * G::LDK + cv * VEC) = zq;
+      *reinterpret_cast<uint4 *>(sK + r * G::LDK + cv * VEC) = zk;
+    }
+  }
+  __syncthreads();
+  // row fragments of this wave's 16 chunk rows (re-read from LDS where used)
+#define QA(ks) M::ld(sQ + (16 * rt + lr) * G::LDK + (ks) * KS + EPL * lg)
+#define KA(ks) M::ld(sK + (16 * rt + lr) * G::LDK + (ks) * KS + EPL * lg)
+  f32x4 qk[2], kk[2];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    qk[cc] = zero4();
+    kk[cc] = zero4();
+  }
+#pragma unroll
+  for (int ks = 0; ks < NKK; ++ks) {
+    const auto qa = QA(ks), ka = KA(ks);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+      if (pc0 + cc <= rt) {
+        const auto kb = M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg);
+        qk[cc] = M::mma(qa, kb, qk[cc]);
+        kk[cc] = M::mma(ka, kb, kk[cc]);
+      }
+  }
+  f32x4 dq_tot[NCHK], dk_tot[NCHK];
+#pragma unroll
+  for (int m = 0; m < NCHK; ++m) {
+    dq_tot[m] = zero4();
+    dk_tot[m] = zero4();
+  }
+
+  for (int hl = 0; hl < Gq; ++hl) {
+    const int h = hq * Gq + hl;
+    const int64_t cg = gid * p.Hv + h;  // (chunk, v-head) slot of per-chunk buffers
+    // ---- per v-head inputs: T, gates
+    {
+      const E *tm = tmat + cg * 64 * 64;
+      constexpr int VEC = G::VEC, PT = 64 / VEC;
+      for (int idx = tid; idx < 64 * PT; idx += kThreads) {
+        const int r = idx / PT, cv = idx % PT;
+        *reinterpret_cast<uint4 *>(sT + r * G::LDC + cv * VEC) =
+            *reinterpret_cast<const uint4 *>(tm + r * 64 + cv * VEC);
+      }
+      if (tid < 64) {
+        const int64_t gi = (tok0 + tid) * p.Hv + h;
+        const float gv = tid < rows ? a.g[gi] : 0.f;
+        const float bv = tid < rows ? to_f32(bp[gi]) : 0.f;
+        const float gam = wave_incl_scan(gv);
+        const float gL = __shfl(gam, 63, 64);
+        sgam[tid] = gam;
+        seg[tid] = expf(gam);
+        sdec[tid] = expf(gL - gam);
+        sbet[tid] = bv;
+      }
+    }
+    __syncthreads();
+    float gam_s[4], eg_s[4], dec_s[4], bet_s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 16 * rt + 4 * lg + i;
+      gam_s[i] = sgam[s];
+      eg_s[i] = seg[s];
+      dec_s[i] = sdec[s];
+      bet_s[i] = sbet[s];
+    }
+    // P^T (P = lower_incl(Q K^T * E)) of this v-head into LDS
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int t = 16 * (pc0 + cc) + lr;
+      const float gt = sgam[t];
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * rt + 4 * lg + i;
+        pv[i] = (t <= s) ? qk[cc][i] * expf(gam_s[i] - gt) : 0.f;
+      }
+      st4(sPt + t * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
+    }
+    f32x4 dq1[NCHK], dk2[NCHK], dk3[NCHK], dp[2], da[2];
+#pragma unroll
+    for (int m = 0; m < NCHK; ++m) {
+      dq1[m] = zero4();
+      dk2[m] = zero4();
+      dk3[m] = zero4();
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      dp[cc] = zero4();
+      da[cc] = zero4();
+    }
+    float de_p[4] = {0.f, 0.f, 0.f, 0.f}, db_p[4] = {0.f, 0.f, 0.f, 0.f};
+    float gl_p = 0.f;
+    const float *hs = hst + cg * (int64_t)K * V;
+    const float *ds = dst + cg * (int64_t)K * V;
+
+    for (int vb = 0; vb < C::NVB; ++vb) {
+      const int v0 = vb * VB;
+      __syncthreads();  // previous readers of the block buffers are done
+      // S, D blocks (fp32 -> element type), <D, S> partial, dO block
+      for (int idx = tid; idx < K * (VB / 4); idx += kThreads) {
+        const int i = idx / (VB / 4), j4 = (idx % (VB / 4)) * 4;
+        const float4 s4 = *reinterpret_cast<const float4 *>(hs + (int64_t)i * V + v0 + j4);
+        const float4 d4 = *reinterpret_cast<const float4 *>(ds + (int64_t)i * V + v0 + j4);
+        gl_p += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
+        st4(sS + i * LDB + j4, s4.x, s4.y, s4.z, s4.w);
+        st4(sD + i * LDB + j4, d4.x, d4.y, d4.z, d4.w);
+      }
+      {
+        constexpr int VEC = G::VEC, PB = VB / VEC;
+        for (int idx = tid; idx < 64 * PB; idx += kThreads) {
+          const int r = idx / PB, cv = idx % PB;
+          uint4 z = make_uint4(0u, 0u, 0u, 0u);
+          if (r < rows)
+            z = *reinterpret_cast<const uint4 *>(dop + ((tok0 + r) * p.Hv + h) * V + v0 +
+                                                 cv * VEC);
+          *reinterpret_cast<uint4 *>(sDO + r * LDB + cv * VEC) = z;
+        }
+      }
+      float vv[NCHB][4];
+#pragma unroll
+      for (int m = 0; m < NCHB; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * rt + 4 * lg + i;
+          const int vc = 16 * (ch * NCHB + m) + lr;
+          vv[m][i] = s < rows ? to_f32(vp[((tok0 + s) * p.Hv + h) * V + v0 + vc]) : 0.f;
+        }
+      __syncthreads();
+      // ---- phase 2: K S, Q S; R; dO S^T
+      f32x4 ks_[NCHB], qs_[NCHB];
+#pragma unroll
+      for (int m = 0; m < NCHB; ++m) {
+        ks_[m] = zero4();
+        qs_[m] = zero4();
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKK; ++ks) {
+        const auto qa = QA(ks), ka = KA(ks);
+#pragma unroll
+        for (int m = 0; m < NCHB; ++m) {
+          const auto b = M::ld_strided(sS + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB);
+          ks_[m] = M::mma(ka, b, ks_[m]);
+          qs_[m] = M::mma(qa, b, qs_[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NCHB; ++m) {
+        const int vc = 16 * (ch * NCHB + m) + lr;
+        float rr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * rt + 4 * lg + i;
+          rr[i] = bet_s[i] * (vv[m][i] - eg_s[i] * ks_[m][i]);
+          de_p[i] += scale * to_f32(sDO[s * LDB + vc]) * qs_[m][i];
+        }
+        st4(sRt + vc * G::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKB; ++ks) {
+        const auto da_ = M::ld(sDO + (16 * rt + lr) * LDB + ks * KS + EPL * lg);
+#pragma unroll
+        for (int m = 0; m < NCHK; ++m)
+          dq1[m] = M::mma(da_, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+                          dq1[m]);
+      }
+      __syncthreads();
+      // ---- phase 3: Vn = T R; K D
+      {
+        f32x4 vn[NCHB], kd[NCHB];
+#pragma unroll
+        for (int m = 0; m < NCHB; ++m) {
+          vn[m] = zero4();
+          kd[m] = zero4();
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKC; ++ks) {
+          const auto ta = M::ld(sT + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+#pragma unroll
+          for (int m = 0; m < NCHB; ++m)
+            vn[m] = M::mma(ta,
+                           M::ld(sRt + (16 * (ch * NCHB + m) + lr) * G::LDC + ks * KS + EPL * lg),
+                           vn[m]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKK; ++ks)
+#pragma unroll
+          for (int m = 0; m < NCHB; ++m)
+            kd[m] = M::mma(KA(ks),
+                           M::ld_strided(sD + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB),
+                           kd[m]);
+        __syncthreads();  // R^T fully consumed before dVn^T overwrites it
+#pragma unroll
+        for (int m = 0; m < NCHB; ++m) {
+          const int vc = 16 * (ch * NCHB + m) + lr;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sVn[(16 * rt + 4 * lg + i) * LDB + vc] = from_f32<E>(vn[m][i]);
+        }
+        // ---- phase 4a: dVn = dec * (K D) + scale P^T dO
+        f32x4 x[NCHB];
+#pragma unroll
+        for (int m = 0; m < NCHB; ++m) x[m] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKC; ++ks) {
+          const auto pa = M::ld(sPt + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+#pragma unroll
+          for (int m = 0; m < NCHB; ++m)
+            x[m] = M::mma(pa,
+                          M::ld_strided(sDO + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB),
+                          x[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < NCHB; ++m) {
+          const int vc = 16 * (ch * NCHB + m) + lr;
+          float y[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = dec_s[i] * kd[m][i] + scale * x[m][i];
+          st4(sDVnt + vc * G::LDC + 16 * rt + 4 * lg, y[0], y[1], y[2], y[3]);
+        }
+      }
+      __syncthreads();
+      // ---- phase 4b: Vn D^T;  phase 5: dR = T^T dVn, dv, dbeta / de rows
+#pragma unroll
+      for (int ks = 0; ks < NKB; ++ks) {
+        const auto vna = M::ld(sVn + (16 * rt + lr) * LDB + ks * KS + EPL * lg);
+#pragma unroll
+        for (int m = 0; m < NCHK; ++m)
+          dk3[m] = M::mma(vna, M::ld(sD + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+                          dk3[m]);
+      }
+      f32x4 dr[NCHB];
+#pragma unroll
+      for (int m = 0; m < NCHB; ++m) dr[m] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKC; ++ks) {
+        const auto tta = M::ld_strided(sT + (ks * KS + EPL * lg) * G::LDC + 16 * rt + lr, G::LDC);
+#pragma unroll
+        for (int m = 0; m < NCHB; ++m)
+          dr[m] = M::mma(tta,
+                         M::ld(sDVnt + (16 * (ch * NCHB + m) + lr) * G::LDC + ks * KS + EPL * lg),
+                         dr[m]);
+      }
+      __syncthreads();  // D block fully consumed before dR overwrites it
+#pragma unroll
+      for (int m = 0; m < NCHB; ++m) {
+        const int vc = 16 * (ch * NCHB + m) + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * rt + 4 * lg + i;
+          const float x = dr[m][i];
+          sDR[s * LDB + vc] = from_f32<E>(x);
+          if (s < rows) dvp[((tok0 + s) * p.Hv + h) * V + v0 + vc] = from_f32<E>(bet_s[i] * x);
+          db_p[i] += x * (vv[m][i] - eg_s[i] * ks_[m][i]);
+          de_p[i] -= bet_s[i] * x * ks_[m][i];
+        }
+      }
+      __syncthreads();
+      // ---- phase 6: dP += dO Vn^T, dA -= dR Vn^T, dR S^T
+#pragma unroll
+      for (int ks = 0; ks < NKB; ++ks) {
+        const auto doa = M::ld(sDO + (16 * rt + lr) * LDB + ks * KS + EPL * lg);
+        const auto dra = M::ld(sDR + (16 * rt + lr) * LDB + ks * KS + EPL * lg);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+          if (pc0 + cc <= rt) {
+            const auto vnb = M::ld(sVn + (16 * (pc0 + cc) + lr) * LDB + ks * KS + EPL * lg);
+            dp[cc] = M::mma(doa, vnb, dp[cc]);
+            da[cc] = M::mma(dra, vnb, da[cc]);
+          }
+#pragma unroll
+        for (int m = 0; m < NCHK; ++m)
+          dk2[m] = M::mma(dra, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+                          dk2[m]);
+      }
+    }
+    // ---- phase 7: masks, dP*E, dKK, dgamma row/column terms
+    float rs_p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int t = 16 * (pc0 + cc) + lr;
+      const float gt = sgam[t];
+      float pe[4], kkv[4], cs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * rt + 4 * lg + i;
+        const float e = (t <= s) ? expf(gam_s[i] - gt) : 0.f;
+        const float dpm = (t <= s) ? scale * dp[cc][i] : 0.f;
+        const float dam = (t < s) ? -da[cc][i] : 0.f;
+        pe[i] = dpm * e;
+        kkv[i] = bet_s[i] * dam * e;
+        // P_st = QK_st E_st,  A_st = beta_s KK_st E_st
+        const float term = dpm * qk[cc][i] * e + dam * bet_s[i] * kk[cc][i] * e;
+        rs_p[i] += term;
+        cs += term;
+        db_p[i] += dam * kk[cc][i] * e;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * rt + 4 * lg + i;
+        sPE[s * G::LDC + t] = from_f32<E>(pe[i]);
+        sKK[s * G::LDC + t] = from_f32<E>(kkv[i]);
+      }
+      cs += __shfl_xor(cs, 16, 64);
+      cs += __shfl_xor(cs, 32, 64);
+      if (lg == 0) colp[rt][t] = cs;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float de = sum16(de_p[i]), db = sum16(db_p[i]), rs = sum16(rs_p[i]);
+      if (lr == 0) {
+        const int s = 16 * rt + 4 * lg + i;
+        rowp[0][ch][s] = de;
+        rowp[1][ch][s] = db;
+        rowp[2][ch][s] = rs;
+      }
+    }
+    {
+      float gsum = gl_p;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) gsum += __shfl_xor(gsum, o, 64);
+      if (lane == 0) glp[w] = gsum;
+    }
+    __syncthreads();
+    // ---- phase 8: dq, dk contributions of this v-head; c_r
+    {
+      float c_p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < NCHK; ++m) {
+        const int ic = 16 * (ch * NCHK + m) + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * rt + 4 * lg + i;
+          c_p[i] += dec_s[i] * dk3[m][i] * to_f32(sK[s * G::LDK + ic]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float cr = sum16(c_p[i]);
+        if (lr == 0) cpart[ch][16 * rt + 4 * lg + i] = cr;
+      }
+      f32x4 a1[NCHK], a2[NCHK];
+#pragma unroll
+      for (int m = 0; m < NCHK; ++m) {
+        a1[m] = zero4();
+        a2[m] = zero4();
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKC; ++ks) {
+        const int t0 = ks * KS + EPL * lg;
+        const auto pea = M::ld(sPE + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+        const auto peta = M::ld_strided(sPE + t0 * G::LDC + 16 * rt + lr, G::LDC);
+        const auto ma = M::ld_sym(sKK + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg,
+                                  sKK + t0 * G::LDC + 16 * rt + lr, G::LDC);
+#pragma unroll
+        for (int m = 0; m < NCHK; ++m) {
+          const int ic = 16 * (ch * NCHK + m) + lr;
+          const auto kb = M::ld_strided(sK + t0 * G::LDK + ic, G::LDK);
+          const auto qb = M::ld_strided(sQ + t0 * G::LDK + ic, G::LDK);
+          a1[m] = M::mma(pea, kb, a1[m]);   // (dP*E) K
+          a2[m] = M::mma(peta, qb, a2[m]);  // (dP*E)^T Q
+          a2[m] = M::mma(ma, kb, a2[m]);    // (dKK + dKK^T) K
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NCHK; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dq_tot[m][i] += scale * eg_s[i] * dq1[m][i] + a1[m][i];
+          dk_tot[m][i] += -bet_s[i] * eg_s[i] * dk2[m][i] + dec_s[i] * dk3[m][i] + a2[m][i];
+        }
+    }
+    __syncthreads();
+    // ---- phase 9: dbeta, dgamma -> dg (reverse cumsum inside the chunk)
+    if (w == 0) {
+      const int r = lane;
+      const float cr = cpart[0][r] + cpart[1][r];
+      float csum = cr;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) csum += __shfl_xor(csum, o, 64);
+      float gl = 0.f;
+#pragma unroll
+      for (int i = 0; i < kNW; ++i) gl += glp[i];
+      const float de = rowp[0][0][r] + rowp[0][1][r];
+      const float db = rowp[1][0][r] + rowp[1][1][r];
+      const float rs = rowp[2][0][r] + rowp[2][1][r];
+      const float cs = colp[0][r] + colp[1][r] + colp[2][r] + colp[3][r];
+      float dgam = seg[r] * de + rs - cs - cr;
+      if (r == rows - 1) dgam += csum + seg[63] * gl;
+      if (r >= rows) dgam = 0.f;
+      // reverse inclusive scan: dg_r = sum_{r' >= r} dgam_r'
+      float x = dgam;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_down(x, d, 64);
+        if (r + d < 64) x += y;
+      }
+      if (r < rows) {
+        const int64_t gi = (tok0 + r) * p.Hv + h;
+        a.dg[gi] = x;
+        dbp[gi] = from_f32<E>(db);
+      }
+    }
+    __syncthreads();
+  }
+#undef QA
+#undef KA
+  // ---- dq, dk of the q/k head (sum over its v-heads in order)
+#pragma unroll
+  for (int m = 0; m < NCHK; ++m) {
+    const int ic = 16 * (ch * NCHK + m) + lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 16 * rt + 4 * lg + i;
+      if (s < rows) {
+        const int64_t off = ((tok0 + s) * p.Hq + hq) * K + ic;
+        dqp[off] = from_f32<E>(dq_tot[m][i]);
+        dkp[off] = from_f32<E>(dk_tot[m][i]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+template <typename E, int K, int V>
+static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
+  const Problem &p = a.p;
+  const Plan &pl = a.plan;
+  FwdArgs fa;
+  fa.p = p;
+  fa.plan = pl;
+  fa.q = a.q;
+  fa.k = a.k;
+  fa.v = a.v;
+  fa.beta = a.beta;
+  fa.g = a.g;
+  fa.h0 = a.h0;
+  fa.o = nullptr;
+  fa.ht = nullptr;
+  fa.g_cum = nullptr;
+  fa.A = nullptr;
+  fa.h = reinterpret_cast<float *>(a.ws + a.wl.hstates);
+  fa.ws = a.ws;
+  fa.wl = a.wl.fwd;
+  hipError_t e = launch_fwd_states(fa, a.A, st);
+  if (e != hipSuccess) return e;
+  if (pl.total_chunks > 0) {
+    rev_segment_kernel<E, K, V, kRMain>
+        <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);
+    if (pl.max_segs_per_seq > 1)
+      rev_segment_kernel<E, K, V, kRFix>
+          <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);
+  }
+  if (pl.max_segs_per_seq > 1 || pl.has_empty)
+    rev_serial_kernel<E, K, V><<<dim3((unsigned)(p.N * p.Hv)), kThreads, 0, st>>>(a);
+  if (pl.total_chunks > 0)
+    local_grad_kernel<E, K, V><<<dim3((unsigned)(pl.total_chunks * p.Hq)), kThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t st) {
+  const int K = a.p.K, V = a.p.V;
+#define GDN_KV(E, KK, VV) \
+  if (K == KK && V == VV) return launch_bwd_t<E, KK, VV>(a, st);
+  if (a.p.dtype == 1) {
+    GDN_KV(bf16, 128, 128)
+    GDN_KV(bf16, 64, 64)
+    GDN_KV(bf16, 32, 32)
+    GDN_KV(bf16, 64, 128)
+    GDN_KV(bf16, 128, 64)
+  } else {
+    GDN_KV(float, 32, 32)
+    GDN_KV(float, 64, 64)
+    GDN_KV(float, 32, 64)
+    GDN_KV(float, 64, 32)
+  }
+#undef GDN_KV
+  return hipErrorInvalidValue;
+}
 
 }  // namespace gdn

@@ -51,6 +51,20 @@ struct Mma<bf16> {
     for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)p[e * stride] * w[e]);
     return f;
   }
+  // 8 elements at stride `stride`
+  __device__ static __forceinline__ frag ld_strided(const bf16 *p, int stride) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = p[e * stride];
+    return f;
+  }
+  // 8 contiguous elements of p plus 8 strided elements of q (sum, rounded)
+  __device__ static __forceinline__ frag ld_sym(const bf16 *p, const bf16 *q, int stride) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)p[e] + (float)q[e * stride]);
+    return f;
+  }
 };
 
 template <>
@@ -65,6 +79,10 @@ struct Mma<float> {
   __device__ static __forceinline__ frag ld_strided_scaled(const float *p, int stride,
                                                   const float *w) {
     return p[0] * w[0];
+  }
+  __device__ static __forceinline__ frag ld_strided(const float *p, int stride) { return p[0]; }
+  __device__ static __forceinline__ frag ld_sym(const float *p, const float *q, int stride) {
+    return p[0] + q[0];
   }
 };
 

@@ -74,6 +74,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+// states only (a.h), no output; T from Ain ([B,T,Hv,64] fp32) when given
+hipError_t launch_fwd_states(const FwdArgs &a, const float *Ain, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 int run_selftest();
 

@@ -1,0 +1,311 @@
+// Machinery shared by the segment kernels of the forward and the backward:
+// locating a chunk / segment of a (possibly packed) batch, the register
+// prefetch of one chunk's inputs, and the K x V fp32 state held as 16x16
+// accumulator tiles spread over the waves of a workgroup.
+#pragma once
+
+#include "gdn_common.hpp"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+constexpr int kNW = 8;              // waves per segment workgroup
+constexpr int kThreads = 64 * kNW;  // 512
+
+struct SeqInfo {
+  int64_t tok0;  // first token (flat index into the [B*T] token axis)
+  int len;
+  int nchunks;
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const Problem &p, int n) {
+  SeqInfo s;
+  if (p.cu) {
+    s.tok0 = p.cu[n];
+    s.len = p.cu[n + 1] - p.cu[n];
+  } else {
+    s.tok0 = (int64_t)n * p.T;
+    s.len = p.T;
+  }
+  s.nchunks = (s.len + kChunk - 1) / kChunk;
+  return s;
+}
+
+// Chunk `gid` (global, token order) -> sequence and chunk index inside it.
+struct ChunkLoc {
+  int n, c;
+  SeqInfo si;
+};
+
+__device__ __forceinline__ ChunkLoc locate_chunk(const Problem &p, const int32_t *chunk_prefix,
+                                                 int64_t gid) {
+  ChunkLoc l;
+  if (!p.cu) {
+    const int nc = (p.T + kChunk - 1) / kChunk;
+    l.n = (int)(gid / nc);
+    l.c = (int)(gid % nc);
+  } else {
+    l.n = find_seq(chunk_prefix, p.N, gid);
+    l.c = (int)(gid - chunk_prefix[l.n]);
+  }
+  l.si = seq_info(p, l.n);
+  return l;
+}
+
+// Segment `sg` -> sequence, segment index j, chunk range, first chunk id.
+struct SegLoc {
+  int n, j, nseg;
+  SeqInfo si;
+  int64_t chunk0;  // global id of the sequence's first chunk
+  int64_t seg0;    // global id of the sequence's first segment
+  int c_begin, c_end;
+};
+
+__device__ __forceinline__ SegLoc locate_segment(const Problem &p, int seg_chunks,
+                                                 const int32_t *chunk_prefix,
+                                                 const int32_t *seg_prefix, int64_t sg) {
+  SegLoc l;
+  if (!p.cu) {
+    const int nc = (p.T + kChunk - 1) / kChunk;
+    l.nseg = (nc + seg_chunks - 1) / seg_chunks;
+    l.n = (int)(sg / l.nseg);
+    l.j = (int)(sg % l.nseg);
+    l.chunk0 = (int64_t)l.n * nc;
+    l.seg0 = (int64_t)l.n * l.nseg;
+  } else {
+    l.n = find_seq(seg_prefix, p.N, sg);
+    l.j = (int)(sg - seg_prefix[l.n]);
+    l.nseg = seg_prefix[l.n + 1] - seg_prefix[l.n];
+    l.chunk0 = chunk_prefix[l.n];
+    l.seg0 = seg_prefix[l.n];
+  }
+  l.si = seq_info(p, l.n);
+  l.c_begin = l.j * seg_chunks;
+  l.c_end = min(l.c_begin + seg_chunks, l.si.nchunks);
+  return l;
+}
+
+// Same for a (sequence n) without a segment id (serial passes).
+__device__ __forceinline__ SegLoc locate_sequence(const Problem &p, int seg_chunks,
+                                                  const int32_t *chunk_prefix,
+                                                  const int32_t *seg_prefix, int n) {
+  SegLoc l;
+  l.n = n;
+  l.j = 0;
+  l.si = seq_info(p, n);
+  if (!p.cu) {
+    const int nc = (p.T + kChunk - 1) / kChunk;
+    l.nseg = (nc + seg_chunks - 1) / seg_chunks;
+    l.chunk0 = (int64_t)n * nc;
+    l.seg0 = (int64_t)n * l.nseg;
+  } else {
+    l.nseg = seg_prefix[n + 1] - seg_prefix[n];
+    l.chunk0 = chunk_prefix[n];
+    l.seg0 = seg_prefix[n];
+  }
+  l.c_begin = 0;
+  l.c_end = l.si.nchunks;
+  return l;
+}
+
+// Tile geometry of the segment kernels.
+template <typename E, int K, int V>
+struct Geo {
+  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int LDK = K + PAD;   // rows of length K
+  static constexpr int LDV = V + PAD;   // rows of length V
+  static constexpr int LDC = 64 + PAD;  // rows of length 64 (chunk)
+  static constexpr int NCT = V / 16;    // 16-wide column tiles over V
+  static constexpr int NRT = K / 16;    // 16-high row tiles over K
+  static constexpr int NCH = NCT / 2;   // column tiles per half
+  // state tiles: wave w owns tiles w*NTS .. w*NTS+NTS-1 (row-major over
+  // NRT x NCT); all of them share one row tile.
+  static constexpr int NT = NRT * NCT;
+  static constexpr int NTS = (NT + kNW - 1) / kNW;
+  __device__ static bool owns(int w) { return w * NTS < NT; }
+  __device__ static int srt(int w) { return (w * NTS) / NCT; }
+  __device__ static int sct(int w) { return (w * NTS) % NCT; }
+  // chunk-input prefetch: 16-byte pieces
+  static constexpr int VEC = 16 / (int)sizeof(E);
+  static constexpr int PQ = 64 * K / VEC;   // pieces of a 64 x K tile
+  static constexpr int PV = 64 * V / VEC;   // pieces of a 64 x V tile
+  static constexpr int PT = 64 * 64 / VEC;  // pieces of a 64 x 64 tile
+  static constexpr int NQ = (PQ + kThreads - 1) / kThreads;
+  static constexpr int NV = (PV + kThreads - 1) / kThreads;
+  static constexpr int NTM = (PT + kThreads - 1) / kThreads;
+};
+
+template <typename E, int K, int V>
+struct Pref {
+  using G = Geo<E, K, V>;
+  uint4 q[G::NQ], k[G::NQ], v[G::NV], t[G::NTM];
+  float g, b;
+  int rows;
+};
+
+// Load one chunk's q, k, (v-like tile), T, g, beta into registers.
+// vsrc is v (forward) or do (backward); it is skipped when null-like (want_v).
+template <typename E, int K, int V, bool WANT_V>
+__device__ __forceinline__ void pref_load(Pref<E, K, V> &pf, const Problem &p, const E *qp,
+                                          const E *kp, const E *vsrc, const E *tmat,
+                                          const float *g, const E *beta, int64_t tok0,
+                                          int rows, int h, int64_t cgid) {
+  using G = Geo<E, K, V>;
+  const int tid = threadIdx.x;
+  const int hq = h / (p.Hv / p.Hq);
+  constexpr int PK = K / G::VEC, PVr = V / G::VEC;
+  pf.rows = rows;
+#pragma unroll
+  for (int m = 0; m < G::NQ; ++m) {
+    const int idx = tid + kThreads * m;
+    const int r = idx / PK, cv = idx % PK;
+    uint4 zq = make_uint4(0u, 0u, 0u, 0u), zk = zq;
+    if (idx < G::PQ && r < rows) {
+      const int64_t off = ((tok0 + r) * p.Hq + hq) * K + cv * G::VEC;
+      zq = *reinterpret_cast<const uint4 *>(qp + off);
+      zk = *reinterpret_cast<const uint4 *>(kp + off);
+    }
+    pf.q[m] = zq;
+    pf.k[m] = zk;
+  }
+  if (WANT_V) {
+#pragma unroll
+    for (int m = 0; m < G::NV; ++m) {
+      const int idx = tid + kThreads * m;
+      const int r = idx / PVr, cv = idx % PVr;
+      uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      if (idx < G::PV && r < rows)
+        z = *reinterpret_cast<const uint4 *>(vsrc + ((tok0 + r) * p.Hv + h) * V +
+                                             cv * G::VEC);
+      pf.v[m] = z;
+    }
+  }
+  const E *tm = tmat + (cgid * p.Hv + h) * 64 * 64;
+#pragma unroll
+  for (int m = 0; m < G::NTM; ++m) {
+    const int idx = tid + kThreads * m;
+    uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    if (idx < G::PT) z = *reinterpret_cast<const uint4 *>(tm + idx * G::VEC);
+    pf.t[m] = z;
+  }
+  pf.g = 0.f;
+  pf.b = 0.f;
+  if (tid < 64 && tid < rows) {
+    const int64_t gi = (tok0 + tid) * p.Hv + h;
+    pf.g = g[gi];
+    pf.b = to_f32(beta[gi]);
+  }
+}
+
+// Per-chunk gate quantities in LDS.
+struct GateLds {
+  float *gam;  // inclusive cumsum gamma_r
+  float *eg;   // exp(gamma_r)
+  float *dec;  // exp(gamma_L - gamma_r)
+  float *bet;  // beta_r
+};
+
+// Wave 0 turns the prefetched g, beta into the gate quantities.
+__device__ __forceinline__ void gate_commit(float g, float b, const GateLds &G) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const float gam = wave_incl_scan(g);
+    const float gL = __shfl(gam, 63, 64);
+    G.gam[tid] = gam;
+    G.eg[tid] = expf(gam);
+    G.dec[tid] = expf(gL - gam);
+    G.bet[tid] = b;
+  }
+}
+
+// ----- fp32 K x V state as register tiles (owned tiles of Geo) -----
+template <int N>
+using Tiles = TileArr<N>;
+
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_zero(Tiles<Geo<E, K, V>::NTS> &s) {
+#pragma unroll
+  for (int m = 0; m < Geo<E, K, V>::NTS; ++m) s[m] = zero4();
+}
+
+// Read a global fp32 [K][V] matrix (or zeros if src is null) into the tiles.
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_load(Tiles<Geo<E, K, V>::NTS> &s, const float *src) {
+  using G = Geo<E, K, V>;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < G::NTS; ++m) {
+    f32x4 x = zero4();
+    if (src && G::owns(w)) {
+      const int rt = G::srt(w), ct = G::sct(w) + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = src[(16 * rt + 4 * lg + i) * V + 16 * ct + lr];
+    }
+    s[m] = x;
+  }
+}
+
+// dst = tiles (+ add[] if given) (+ dst if accumulate).
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_store(const Tiles<Geo<E, K, V>::NTS> &s, float *dst,
+                                            const float *add, bool accumulate) {
+  using G = Geo<E, K, V>;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  if (!G::owns(w)) return;
+  const int rt = G::srt(w);
+#pragma unroll
+  for (int m = 0; m < G::NTS; ++m) {
+    const int ct = G::sct(w) + m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = (16 * rt + 4 * lg + i) * V + 16 * ct + lr;
+      float x = s[m][i];
+      if (add) x += add[off];
+      if (accumulate) x += dst[off];
+      dst[off] = x;
+    }
+  }
+}
+
+// Transposed working copy (element type) in LDS: dstT[v][i] = S[i][v].
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_to_lds_t(const Tiles<Geo<E, K, V>::NTS> &s, E *dstT) {
+  using G = Geo<E, K, V>;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  if (!G::owns(w)) return;
+  const int rt = G::srt(w);
+#pragma unroll
+  for (int m = 0; m < G::NTS; ++m) {
+    const int ct = G::sct(w) + m;
+    st4(dstT + (16 * ct + lr) * G::LDK + 16 * rt + 4 * lg, s[m][0], s[m][1], s[m][2],
+        s[m][3]);
+  }
+}
+
+template <typename E, int K, int V>
+__device__ __forceinline__ bool tiles_nonzero(const Tiles<Geo<E, K, V>::NTS> &s) {
+  bool nz = false;
+#pragma unroll
+  for (int m = 0; m < Geo<E, K, V>::NTS; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nz |= (s[m][i] != 0.f);
+  return nz;
+}
+
+// Workgroup-wide OR of a per-thread flag (uses 8 ints of LDS).
+__device__ __forceinline__ bool block_any(bool x, int *sflag) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool wx = __any(x);
+  if (lane == 0) sflag[w] = wx ? 1 : 0;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < kNW; ++i) r |= sflag[i];
+  __syncthreads();
+  return r != 0;
+}
+
+}  // namespace gdn
