@@ -74,6 +74,10 @@ def lib():
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_bwd.argtypes = [pp] + [P] * 15 + [P, S, P]
         L.gdn_chunk_bwd.restype = ctypes.c_int
+        L.gdn_timing_enable.argtypes = [ctypes.c_int]
+        L.gdn_timing_enable.restype = ctypes.c_int
+        L.gdn_timing_collect.argtypes = [ctypes.c_int, P, P, P]
+        L.gdn_timing_collect.restype = ctypes.c_int
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_selftest.restype = ctypes.c_int
         _lib = L
@@ -91,6 +95,26 @@ def _check(rc: int):
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def timing_enable(on: bool) -> bool:
+    """Turn per-kernel HIP-event timing on/off for this thread (see gdn.h)."""
+    return bool(lib().gdn_timing_enable(1 if on else 0))
+
+
+def timing_collect(max_kernels: int = 64):
+    """Wait for the recorded kernel events; returns {name: (launches, total_ms)}."""
+    names = ctypes.create_string_buffer(32 * max_kernels)
+    counts = (ctypes.c_int32 * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    n = lib().gdn_timing_collect(max_kernels, names, counts, ms)
+    if n < 0:
+        raise GdnError(-n, last_error())
+    out = {}
+    for i in range(n):
+        nm = names.raw[32 * i:32 * (i + 1)].split(b"\0", 1)[0].decode()
+        out[nm] = (int(counts[i]), float(ms[i]))
+    return out
 
 
 def selftest() -> None:
@@ -148,13 +172,15 @@ def _check_inputs(q, k, v, g, beta):
 
 def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                cu_seqlens=None, output_final_state=True,
-                               return_intermediates=True, cp_mode: int = -1):
+                               return_intermediates=True, cp_mode: int = -1,
+                               return_states: bool = True):
     """Forward.  Returns (g_cum, A, o, h, final_state).
 
     g_cum is the gate cumsum inside each 64-token chunk [B,T,Hv]; A the
     per-chunk inverse T = (I + strict_lower(diag(beta) K K^T * decay))^-1,
     [B,T,Hv,64]; h the state entering every chunk [NC,Hv,K,V].  With
-    return_intermediates=False those three are None (inference mode).
+    return_intermediates=False those three are None (inference mode);
+    return_states=False drops only h (the backward does not take it).
     """
     _check_inputs(q, k, v, g, beta)
     q, k, v, g, beta = (_contig(x) for x in (q, k, v, g, beta))
@@ -176,7 +202,8 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
             nc = B * ((T + CHUNK - 1) // CHUNK)
         g_cum = torch.empty_like(g)
         A = torch.empty(B, T, Hv, CHUNK, device=dev, dtype=torch.float32)
-        h = torch.empty(nc, Hv, K, V, device=dev, dtype=torch.float32)
+        if return_states:
+            h = torch.empty(nc, Hv, K, V, device=dev, dtype=torch.float32)
     L = lib()
     ws_bytes = L.gdn_chunk_fwd_workspace_size(pr.ref())
     if ws_bytes == 0:

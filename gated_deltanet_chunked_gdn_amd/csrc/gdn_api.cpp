@@ -7,7 +7,9 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <map>
 #include <string>
+#include <vector>
 
 #include "../../include/gdn.h"
 #include "gdn_internal.h"
@@ -162,18 +164,17 @@ gdn::BwdWorkspace bwd_layout(const gdn_problem_t *p, const gdn::Plan &pl) {
   w.fwd = fwd_layout(p, pl, 0);
   size_t off = w.fwd.total;
   const size_t kv = (size_t)p->K * p->V * 4;
+  const size_t kve = (size_t)p->K * p->V * (p->dtype == GDN_BF16 ? 2 : 4);
   w.hstates = off;
-  off = align256(off + (size_t)pl.total_chunks * p->Hv * kv);
+  off = align256(off + (size_t)pl.total_chunks * p->Hv * kve);
   w.dstates = off;
-  off = align256(off + (size_t)pl.total_chunks * p->Hv * kv);
+  off = align256(off + (size_t)pl.total_chunks * p->Hv * kve);
   w.dseg = off;
   off = align256(off + (size_t)pl.total_segs * p->Hv * kv);
   w.deseg = off;
   off = align256(off + (size_t)pl.total_segs * p->Hv * kv);
   w.dflags = off;
   off = align256(off + (size_t)pl.total_segs * p->Hv * 4);
-  w.dqk = off;
-  off = align256(off + (size_t)pl.total_chunks * 64 * p->Hv * 2 * p->K * 4);
   w.total = off;
   return w;
 }
@@ -193,9 +194,76 @@ gdn::Problem to_problem(const gdn_problem_t *p) {
   return q;
 }
 
+struct TimedLaunch {
+  const char *name;
+  hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimedLaunch> g_launches;
+
 }  // namespace
 
+namespace gdn {
+
+KernelTimer::KernelTimer(const char *name, hipStream_t stream) : slot_(-1), stream_(stream) {
+  if (!g_timing) return;
+  TimedLaunch t{name, nullptr, nullptr};
+  if (hipEventCreate(&t.start) != hipSuccess) return;
+  if (hipEventCreate(&t.stop) != hipSuccess) {
+    (void)hipEventDestroy(t.start);
+    return;
+  }
+  (void)hipEventRecord(t.start, stream);
+  slot_ = (int)g_launches.size();
+  g_launches.push_back(t);
+}
+
+KernelTimer::~KernelTimer() {
+  if (slot_ >= 0) (void)hipEventRecord(g_launches[slot_].stop, stream_);
+}
+
+}  // namespace gdn
+
 extern "C" {
+
+int gdn_timing_enable(int on) {
+  const int prev = g_timing ? 1 : 0;
+  g_timing = on != 0;
+  return prev;
+}
+
+int gdn_timing_collect(int max_kernels, char *names, int32_t *counts, double *ms_total) {
+  g_err.clear();
+  std::map<std::string, std::pair<int32_t, double>> acc;
+  std::vector<std::string> order;
+  int rc = 0;
+  for (TimedLaunch &t : g_launches) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess)
+      rc = GDN_ERR_HIP;
+    if (!acc.count(t.name)) order.push_back(t.name);
+    auto &e = acc[t.name];
+    e.first += 1;
+    e.second += ms;
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  g_launches.clear();
+  if (rc) return -fail(rc, "timing events could not be read");
+  int n = 0;
+  for (const std::string &k : order) {
+    if (n >= max_kernels) break;
+    if (names) {
+      snprintf(names + 32 * n, 32, "%s", k.c_str());
+    }
+    if (counts) counts[n] = acc[k].first;
+    if (ms_total) ms_total[n] = acc[k].second;
+    ++n;
+  }
+  return n;
+}
+
 
 const char *gdn_last_error(void) { return g_err.c_str(); }
 
@@ -250,6 +318,7 @@ int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   a.g_cum = g_cum;
   a.A = A;
   a.h = h;
+  a.h_e = nullptr;
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
   hipError_t e = gdn::launch_fwd(a, static_cast<hipStream_t>(stream));

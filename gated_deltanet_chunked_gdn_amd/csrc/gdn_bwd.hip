@@ -141,7 +141,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
   const E *dop = reinterpret_cast<const E *>(a.dout);
   const E *bp = reinterpret_cast<const E *>(a.beta);
   const E *tmat = reinterpret_cast<const E *>(a.ws + a.wl.fwd.tmat);
-  float *dstates = reinterpret_cast<float *>(a.ws + a.wl.dstates);
+  E *dstates = reinterpret_cast<E *>(a.ws + a.wl.dstates);
 
   if (c_begin >= c_end)
     return MODE == kRFix ? !block_any(tiles_nonzero<E, K, V>(st), S.flag) : false;
@@ -157,8 +157,8 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
   bool zero_exit = false;
   for (int c = c_end - 1; c >= c_begin && !zero_exit; --c) {
     {
-      float *ds = dstates + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
-      tiles_store<E, K, V>(st, ds, nullptr, MODE == kRFix);
+      E *ds = dstates + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
+      tiles_store_e<E, K, V>(st, ds, MODE == kRFix);
     }
     // ---- phase A: K D (rows of tile rt, half of V); P^T
     typename M::frag ka[NKK];
@@ -445,6 +445,16 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
+// An MFMA A-operand fragment belongs to one matrix row per lane: scaling the
+// fragment by that row's factor scales the product's row.
+__device__ __forceinline__ bf16x8 frag_scale(bf16x8 f, float s) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)((float)f[e] * s);
+  return r;
+}
+__device__ __forceinline__ float frag_scale(float f, float s) { return f * s; }
+
 template <typename E, int K, int V>
 __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   using G = Geo<E, K, V>;
@@ -457,9 +467,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   constexpr int VB = C::VB, LDB = C::LDB, NCHB = C::NCHB, NCHK = C::NCHK;
   __shared__ __attribute__((aligned(16))) char smem_[C::bytes];
   __shared__ float sgam[64], seg[64], sdec[64], sbet[64];
-  __shared__ float rowp[3][2][64];  // [de, db, rs/c][half][row]
+  __shared__ float rowp[4][2][64];  // [de, db, rs, c][half][row]
   __shared__ float colp[4][64];     // [row tile][col]
-  __shared__ float cpart[2][64];
   __shared__ float glp[kNW];
   E *sm = reinterpret_cast<E *>(smem_);
   E *sQ = sm + C::oQ;
@@ -481,6 +490,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   const int lr = lane & 15, lg = lane >> 4;
   const int rt = w & 3, ch = w >> 2;
   const int pc0 = 2 * ch;
+  const int ra = 16 * rt + lr;  // matrix row an A-operand fragment of this lane covers
   const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
   const int hq = (int)(wid % p.Hq);
   const int64_t gid = wid / p.Hq;
@@ -496,16 +506,17 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   const E *dop = reinterpret_cast<const E *>(a.dout);
   const E *bp = reinterpret_cast<const E *>(a.beta);
   const E *tmat = reinterpret_cast<const E *>(a.ws + a.wl.fwd.tmat);
-  const float *hst = reinterpret_cast<const float *>(a.ws + a.wl.hstates);
-  const float *dst = reinterpret_cast<const float *>(a.ws + a.wl.dstates);
+  const E *hst = reinterpret_cast<const E *>(a.ws + a.wl.hstates);
+  const E *dst = reinterpret_cast<const E *>(a.ws + a.wl.dstates);
   E *dqp = reinterpret_cast<E *>(a.dq);
   E *dkp = reinterpret_cast<E *>(a.dk);
   E *dvp = reinterpret_cast<E *>(a.dv);
   E *dbp = reinterpret_cast<E *>(a.dbeta);
+  constexpr int VEC = G::VEC;
 
   // ---- chunk tiles of q and k (shared by the group's v-heads)
   {
-    constexpr int VEC = G::VEC, PK = K / VEC;
+    constexpr int PK = K / VEC;
     for (int idx = tid; idx < 64 * PK; idx += kThreads) {
       const int r = idx / PK, cv = idx % PK;
       uint4 zq = make_uint4(0u, 0u, 0u, 0u), zk = zq;
@@ -519,9 +530,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // row fragments of this wave's 16 chunk rows (re-read from LDS where used)
-#define QA(ks) M::ld(sQ + (16 * rt + lr) * G::LDK + (ks) * KS + EPL * lg)
-#define KA(ks) M::ld(sK + (16 * rt + lr) * G::LDK + (ks) * KS + EPL * lg)
+#define QA(ks) M::ld(sQ + ra * G::LDK + (ks) * KS + EPL * lg)
+#define KA(ks) M::ld(sK + ra * G::LDK + (ks) * KS + EPL * lg)
+  // raw Q K^T and K K^T tiles of this wave (fp32, shared by the v-heads)
   f32x4 qk[2], kk[2];
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
@@ -539,11 +550,12 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         kk[cc] = M::mma(ka, kb, kk[cc]);
       }
   }
-  f32x4 dq_tot[NCHK], dk_tot[NCHK];
+  // dq, dk of the q/k head: every term is accumulated in place
+  f32x4 dq[NCHK], dk[NCHK];
 #pragma unroll
   for (int m = 0; m < NCHK; ++m) {
-    dq_tot[m] = zero4();
-    dk_tot[m] = zero4();
+    dq[m] = zero4();
+    dk[m] = zero4();
   }
 
   for (int hl = 0; hl < Gq; ++hl) {
@@ -552,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     // ---- per v-head inputs: T, gates
     {
       const E *tm = tmat + cg * 64 * 64;
-      constexpr int VEC = G::VEC, PT = 64 / VEC;
+      constexpr int PT = 64 / VEC;
       for (int idx = tid; idx < 64 * PT; idx += kThreads) {
         const int r = idx / PT, cv = idx % PT;
         *reinterpret_cast<uint4 *>(sT + r * G::LDC + cv * VEC) =
@@ -580,6 +592,10 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       dec_s[i] = sdec[s];
       bet_s[i] = sbet[s];
     }
+    // row factors of this lane's A-operand row
+    const float f_q = scale * seg[ra];            // dq  += (scale e^g dO) S^T
+    const float f_r = -sbet[ra] * seg[ra];        // dk  += (-beta e^g dR) S^T
+    const float f_v = sdec[ra];                   // dk  += (e^{gL-g} Vn) D^T
     // P^T (P = lower_incl(Q K^T * E)) of this v-head into LDS
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
@@ -593,37 +609,35 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
       st4(sPt + t * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
     }
-    f32x4 dq1[NCHK], dk2[NCHK], dk3[NCHK], dp[2], da[2];
-#pragma unroll
-    for (int m = 0; m < NCHK; ++m) {
-      dq1[m] = zero4();
-      dk2[m] = zero4();
-      dk3[m] = zero4();
-    }
+    f32x4 dp[2], da[2];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       dp[cc] = zero4();
       da[cc] = zero4();
     }
     float de_p[4] = {0.f, 0.f, 0.f, 0.f}, db_p[4] = {0.f, 0.f, 0.f, 0.f};
+    float c_p[4] = {0.f, 0.f, 0.f, 0.f};
     float gl_p = 0.f;
-    const float *hs = hst + cg * (int64_t)K * V;
-    const float *ds = dst + cg * (int64_t)K * V;
+    const E *hs = hst + cg * (int64_t)K * V;
+    const E *ds = dst + cg * (int64_t)K * V;
 
     for (int vb = 0; vb < C::NVB; ++vb) {
       const int v0 = vb * VB;
       __syncthreads();  // previous readers of the block buffers are done
-      // S, D blocks (fp32 -> element type), <D, S> partial, dO block
-      for (int idx = tid; idx < K * (VB / 4); idx += kThreads) {
-        const int i = idx / (VB / 4), j4 = (idx % (VB / 4)) * 4;
-        const float4 s4 = *reinterpret_cast<const float4 *>(hs + (int64_t)i * V + v0 + j4);
-        const float4 d4 = *reinterpret_cast<const float4 *>(ds + (int64_t)i * V + v0 + j4);
-        gl_p += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
-        st4(sS + i * LDB + j4, s4.x, s4.y, s4.z, s4.w);
-        st4(sD + i * LDB + j4, d4.x, d4.y, d4.z, d4.w);
-      }
+      // S, D blocks, <D, S> partial, dO block
       {
-        constexpr int VEC = G::VEC, PB = VB / VEC;
+        constexpr int PB = VB / VEC;
+        for (int idx = tid; idx < K * PB; idx += kThreads) {
+          const int i = idx / PB, cv = idx % PB;
+          const uint4 s4 = *reinterpret_cast<const uint4 *>(hs + (int64_t)i * V + v0 + cv * VEC);
+          const uint4 d4 = *reinterpret_cast<const uint4 *>(ds + (int64_t)i * V + v0 + cv * VEC);
+          const E *se = reinterpret_cast<const E *>(&s4);
+          const E *de = reinterpret_cast<const E *>(&d4);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) gl_p += to_f32(se[e]) * to_f32(de[e]);
+          *reinterpret_cast<uint4 *>(sS + i * LDB + cv * VEC) = s4;
+          *reinterpret_cast<uint4 *>(sD + i * LDB + cv * VEC) = d4;
+        }
         for (int idx = tid; idx < 64 * PB; idx += kThreads) {
           const int r = idx / PB, cv = idx % PB;
           uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -643,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           vv[m][i] = s < rows ? to_f32(vp[((tok0 + s) * p.Hv + h) * V + v0 + vc]) : 0.f;
         }
       __syncthreads();
-      // ---- phase 2: K S, Q S; R; dO S^T
+      // ---- phase 2: K S, Q S; R; dq += (scale e^g dO) S^T
       f32x4 ks_[NCHB], qs_[NCHB];
 #pragma unroll
       for (int m = 0; m < NCHB; ++m) {
@@ -655,10 +669,12 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         const auto qa = QA(ks), ka = KA(ks);
 #pragma unroll
         for (int m = 0; m < NCHB; ++m) {
-          const auto b = M::ld_strided(sS + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB);
+          const auto b =
+              M::ld_strided(sS + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB);
           ks_[m] = M::mma(ka, b, ks_[m]);
           qs_[m] = M::mma(qa, b, qs_[m]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int m = 0; m < NCHB; ++m) {
@@ -674,14 +690,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
-        const auto da_ = M::ld(sDO + (16 * rt + lr) * LDB + ks * KS + EPL * lg);
+        const auto da_ = frag_scale(M::ld(sDO + ra * LDB + ks * KS + EPL * lg), f_q);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
-          dq1[m] = M::mma(da_, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
-                          dq1[m]);
+          dq[m] = M::mma(da_, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+                         dq[m]);
       }
       __syncthreads();
-      // ---- phase 3: Vn = T R; K D
+      // ---- phase 3: Vn = T R; K D; c_r = e^{gL-g_r} <Vn_r, (K D)_r>
       {
         f32x4 vn[NCHB], kd[NCHB];
 #pragma unroll
@@ -691,26 +707,32 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int ks = 0; ks < NKC; ++ks) {
-          const auto ta = M::ld(sT + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+          const auto ta = M::ld(sT + ra * G::LDC + ks * KS + EPL * lg);
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
-            vn[m] = M::mma(ta,
-                           M::ld(sRt + (16 * (ch * NCHB + m) + lr) * G::LDC + ks * KS + EPL * lg),
-                           vn[m]);
+            vn[m] = M::mma(
+                ta, M::ld(sRt + (16 * (ch * NCHB + m) + lr) * G::LDC + ks * KS + EPL * lg),
+                vn[m]);
         }
 #pragma unroll
-        for (int ks = 0; ks < NKK; ++ks)
+        for (int ks = 0; ks < NKK; ++ks) {
+          const auto ka = KA(ks);
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
-            kd[m] = M::mma(KA(ks),
-                           M::ld_strided(sD + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB),
-                           kd[m]);
+            kd[m] = M::mma(
+                ka, M::ld_strided(sD + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB),
+                kd[m]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         __syncthreads();  // R^T fully consumed before dVn^T overwrites it
 #pragma unroll
         for (int m = 0; m < NCHB; ++m) {
           const int vc = 16 * (ch * NCHB + m) + lr;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sVn[(16 * rt + 4 * lg + i) * LDB + vc] = from_f32<E>(vn[m][i]);
+          for (int i = 0; i < 4; ++i) {
+            sVn[(16 * rt + 4 * lg + i) * LDB + vc] = from_f32<E>(vn[m][i]);
+            c_p[i] += dec_s[i] * vn[m][i] * kd[m][i];
+          }
         }
         // ---- phase 4a: dVn = dec * (K D) + scale P^T dO
         f32x4 x[NCHB];
@@ -718,12 +740,12 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         for (int m = 0; m < NCHB; ++m) x[m] = zero4();
 #pragma unroll
         for (int ks = 0; ks < NKC; ++ks) {
-          const auto pa = M::ld(sPt + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+          const auto pa = M::ld(sPt + ra * G::LDC + ks * KS + EPL * lg);
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
-            x[m] = M::mma(pa,
-                          M::ld_strided(sDO + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB),
-                          x[m]);
+            x[m] = M::mma(
+                pa, M::ld_strided(sDO + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB),
+                x[m]);
         }
 #pragma unroll
         for (int m = 0; m < NCHB; ++m) {
@@ -735,14 +757,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         }
       }
       __syncthreads();
-      // ---- phase 4b: Vn D^T;  phase 5: dR = T^T dVn, dv, dbeta / de rows
+      // ---- phase 4b: dk += (dec Vn) D^T;  phase 5: dR = T^T dVn, dv, dbeta/de rows
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
-        const auto vna = M::ld(sVn + (16 * rt + lr) * LDB + ks * KS + EPL * lg);
+        const auto vna = frag_scale(M::ld(sVn + ra * LDB + ks * KS + EPL * lg), f_v);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
-          dk3[m] = M::mma(vna, M::ld(sD + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
-                          dk3[m]);
+          dk[m] = M::mma(vna, M::ld(sD + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+                         dk[m]);
       }
       f32x4 dr[NCHB];
 #pragma unroll
@@ -752,9 +774,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         const auto tta = M::ld_strided(sT + (ks * KS + EPL * lg) * G::LDC + 16 * rt + lr, G::LDC);
 #pragma unroll
         for (int m = 0; m < NCHB; ++m)
-          dr[m] = M::mma(tta,
-                         M::ld(sDVnt + (16 * (ch * NCHB + m) + lr) * G::LDC + ks * KS + EPL * lg),
-                         dr[m]);
+          dr[m] = M::mma(
+              tta, M::ld(sDVnt + (16 * (ch * NCHB + m) + lr) * G::LDC + ks * KS + EPL * lg),
+              dr[m]);
       }
       __syncthreads();  // D block fully consumed before dR overwrites it
 #pragma unroll
@@ -771,11 +793,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         }
       }
       __syncthreads();
-      // ---- phase 6: dP += dO Vn^T, dA -= dR Vn^T, dR S^T
+      // ---- phase 6: dP += dO Vn^T, dA -= dR Vn^T, dk += (-beta e^g dR) S^T
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
-        const auto doa = M::ld(sDO + (16 * rt + lr) * LDB + ks * KS + EPL * lg);
-        const auto dra = M::ld(sDR + (16 * rt + lr) * LDB + ks * KS + EPL * lg);
+        const auto doa = M::ld(sDO + ra * LDB + ks * KS + EPL * lg);
+        const auto dra = M::ld(sDR + ra * LDB + ks * KS + EPL * lg);
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
           if (pc0 + cc <= rt) {
@@ -783,10 +805,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
             dp[cc] = M::mma(doa, vnb, dp[cc]);
             da[cc] = M::mma(dra, vnb, da[cc]);
           }
+        const auto drs = frag_scale(dra, f_r);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
-          dk2[m] = M::mma(dra, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
-                          dk2[m]);
+          dk[m] = M::mma(drs, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+                         dk[m]);
       }
     }
     // ---- phase 7: masks, dP*E, dKK, dgamma row/column terms
@@ -823,11 +846,13 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float de = sum16(de_p[i]), db = sum16(db_p[i]), rs = sum16(rs_p[i]);
+      const float cr = sum16(c_p[i]);
       if (lr == 0) {
         const int s = 16 * rt + 4 * lg + i;
         rowp[0][ch][s] = de;
         rowp[1][ch][s] = db;
         rowp[2][ch][s] = rs;
+        rowp[3][ch][s] = cr;
       }
     }
     {
@@ -837,59 +862,29 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       if (lane == 0) glp[w] = gsum;
     }
     __syncthreads();
-    // ---- phase 8: dq, dk contributions of this v-head; c_r
-    {
-      float c_p[4] = {0.f, 0.f, 0.f, 0.f};
+    // ---- phase 8: dq += (dP*E) K;  dk += (dP*E)^T Q + (dKK + dKK^T) K
+#pragma unroll
+    for (int ks = 0; ks < NKC; ++ks) {
+      const int t0 = ks * KS + EPL * lg;
+      const auto pea = M::ld(sPE + ra * G::LDC + ks * KS + EPL * lg);
+      const auto peta = M::ld_strided(sPE + t0 * G::LDC + 16 * rt + lr, G::LDC);
+      const auto ma = M::ld_sym(sKK + ra * G::LDC + ks * KS + EPL * lg,
+                                sKK + t0 * G::LDC + 16 * rt + lr, G::LDC);
 #pragma unroll
       for (int m = 0; m < NCHK; ++m) {
         const int ic = 16 * (ch * NCHK + m) + lr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * rt + 4 * lg + i;
-          c_p[i] += dec_s[i] * dk3[m][i] * to_f32(sK[s * G::LDK + ic]);
-        }
+        const auto kb = M::ld_strided(sK + t0 * G::LDK + ic, G::LDK);
+        const auto qb = M::ld_strided(sQ + t0 * G::LDK + ic, G::LDK);
+        dq[m] = M::mma(pea, kb, dq[m]);
+        dk[m] = M::mma(peta, qb, dk[m]);
+        dk[m] = M::mma(ma, kb, dk[m]);
+        __builtin_amdgcn_sched_barrier(0);  // bound the gathers in flight
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float cr = sum16(c_p[i]);
-        if (lr == 0) cpart[ch][16 * rt + 4 * lg + i] = cr;
-      }
-      f32x4 a1[NCHK], a2[NCHK];
-#pragma unroll
-      for (int m = 0; m < NCHK; ++m) {
-        a1[m] = zero4();
-        a2[m] = zero4();
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKC; ++ks) {
-        const int t0 = ks * KS + EPL * lg;
-        const auto pea = M::ld(sPE + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
-        const auto peta = M::ld_strided(sPE + t0 * G::LDC + 16 * rt + lr, G::LDC);
-        const auto ma = M::ld_sym(sKK + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg,
-                                  sKK + t0 * G::LDC + 16 * rt + lr, G::LDC);
-#pragma unroll
-        for (int m = 0; m < NCHK; ++m) {
-          const int ic = 16 * (ch * NCHK + m) + lr;
-          const auto kb = M::ld_strided(sK + t0 * G::LDK + ic, G::LDK);
-          const auto qb = M::ld_strided(sQ + t0 * G::LDK + ic, G::LDK);
-          a1[m] = M::mma(pea, kb, a1[m]);   // (dP*E) K
-          a2[m] = M::mma(peta, qb, a2[m]);  // (dP*E)^T Q
-          a2[m] = M::mma(ma, kb, a2[m]);    // (dKK + dKK^T) K
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < NCHK; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dq_tot[m][i] += scale * eg_s[i] * dq1[m][i] + a1[m][i];
-          dk_tot[m][i] += -bet_s[i] * eg_s[i] * dk2[m][i] + dec_s[i] * dk3[m][i] + a2[m][i];
-        }
     }
-    __syncthreads();
     // ---- phase 9: dbeta, dgamma -> dg (reverse cumsum inside the chunk)
     if (w == 0) {
       const int r = lane;
-      const float cr = cpart[0][r] + cpart[1][r];
+      const float cr = rowp[3][0][r] + rowp[3][1][r];
       float csum = cr;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) csum += __shfl_xor(csum, o, 64);
@@ -929,8 +924,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       const int s = 16 * rt + 4 * lg + i;
       if (s < rows) {
         const int64_t off = ((tok0 + s) * p.Hq + hq) * K + ic;
-        dqp[off] = from_f32<E>(dq_tot[m][i]);
-        dkp[off] = from_f32<E>(dk_tot[m][i]);
+        dqp[off] = from_f32<E>(dq[m][i]);
+        dkp[off] = from_f32<E>(dk[m][i]);
       }
     }
   }
@@ -954,22 +949,32 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   fa.ht = nullptr;
   fa.g_cum = nullptr;
   fa.A = nullptr;
-  fa.h = reinterpret_cast<float *>(a.ws + a.wl.hstates);
+  fa.h = nullptr;
+  fa.h_e = a.ws + a.wl.hstates;
   fa.ws = a.ws;
   fa.wl = a.wl.fwd;
   hipError_t e = launch_fwd_states(fa, a.A, st);
   if (e != hipSuccess) return e;
   if (pl.total_chunks > 0) {
-    rev_segment_kernel<E, K, V, kRMain>
-        <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);
-    if (pl.max_segs_per_seq > 1)
+    {
+      KernelTimer kt("rev_main", st);
+      rev_segment_kernel<E, K, V, kRMain>
+          <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);
+    }
+    if (pl.max_segs_per_seq > 1) {
+      KernelTimer kt("rev_fix", st);
       rev_segment_kernel<E, K, V, kRFix>
           <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);
+    }
   }
-  if (pl.max_segs_per_seq > 1 || pl.has_empty)
+  if (pl.max_segs_per_seq > 1 || pl.has_empty) {
+    KernelTimer kt("rev_serial", st);
     rev_serial_kernel<E, K, V><<<dim3((unsigned)(p.N * p.Hv)), kThreads, 0, st>>>(a);
-  if (pl.total_chunks > 0)
+  }
+  if (pl.total_chunks > 0) {
+    KernelTimer kt("local_grad", st);
     local_grad_kernel<E, K, V><<<dim3((unsigned)(pl.total_chunks * p.Hq)), kThreads, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

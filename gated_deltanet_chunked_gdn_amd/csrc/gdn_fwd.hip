@@ -331,6 +331,10 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       float *hs = a.h + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
       tiles_store<E, K, V>(st, hs, nullptr, MODE == kFix);
     }
+    if (a.h_e) {
+      E *hs = reinterpret_cast<E *>(a.h_e) + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
+      tiles_store_e<E, K, V>(st, hs, MODE == kFix);
+    }
     // ---- phase A: Q S, K S (this wave's row tile, its half of V), Q K^T
     typename M::frag qa[NKK], ka[NKK];
 #pragma unroll
@@ -613,6 +617,7 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
   const Problem &p = a.p;
   const Plan &pl = a.plan;
   if (Ain) {
+    KernelTimer kt("tmat_from_a", st);
     tmat_from_a_kernel<E><<<dim3((unsigned)(pl.total_chunks * p.Hv)), 64, 0, st>>>(a, Ain);
     return;
   }
@@ -620,6 +625,7 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
   const int G = p.Hv / p.Hq;
   const int nw = G < 4 ? G : 4;
   const size_t lds = (size_t)(C::bytesK > nw * C::bytesA ? C::bytesK : nw * C::bytesA);
+  KernelTimer kt("prep", st);
   prep_kernel<E, K><<<dim3((unsigned)(pl.total_chunks * p.Hq)), 64 * nw, lds, st>>>(a);
 }
 
@@ -627,20 +633,29 @@ template <typename E, int K, int V, bool WRITE_O>
 static hipError_t launch_fwd_t(const FwdArgs &a, const float *Ain, hipStream_t st) {
   const Problem &p = a.p;
   const Plan &pl = a.plan;
-  if (p.cu)
+  if (p.cu) {
+    KernelTimer kt("plan", st);
     plan_kernel<<<1, 64, 0, st>>>(p, pl.seg_chunks,
                                   reinterpret_cast<int32_t *>(a.ws + a.wl.chunk_prefix),
                                   reinterpret_cast<int32_t *>(a.ws + a.wl.seg_prefix));
+  }
   if (pl.total_chunks > 0) {
     launch_prep<E, K>(a, Ain, st);
-    segment_kernel<E, K, V, kMain, WRITE_O>
-        <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);
-    if (pl.max_segs_per_seq > 1)
+    {
+      KernelTimer kt(WRITE_O ? "fwd_main" : "state_main", st);
+      segment_kernel<E, K, V, kMain, WRITE_O>
+          <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);
+    }
+    if (pl.max_segs_per_seq > 1) {
+      KernelTimer kt(WRITE_O ? "fwd_fix" : "state_fix", st);
       segment_kernel<E, K, V, kFix, WRITE_O>
           <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);
+    }
   }
-  if (pl.max_segs_per_seq > 1 || pl.has_empty)
+  if (pl.max_segs_per_seq > 1 || pl.has_empty) {
+    KernelTimer kt(WRITE_O ? "fwd_serial" : "state_serial", st);
     serial_kernel<E, K, V, WRITE_O><<<dim3((unsigned)(p.N * p.Hv)), kThreads, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -35,12 +35,11 @@ struct FwdWorkspace {
 
 struct BwdWorkspace {
   FwdWorkspace fwd;  // forward state recompute (its own pieces)
-  size_t hstates = 0;   // fp32 [NC][Hv][K][V]: state entering each chunk
-  size_t dstates = 0;   // fp32 [NC][Hv][K][V]: gradient w.r.t. state leaving each chunk
+  size_t hstates = 0;   // element type [NC][Hv][K][V]: state entering each chunk
+  size_t dstates = 0;   // element type [NC][Hv][K][V]: gradient of the state leaving each chunk
   size_t dseg = 0;      // fp32 [NS][Hv][K][V]: reverse segment partials
   size_t deseg = 0;     // fp32 [NS][Hv][K][V]
   size_t dflags = 0;    // int32 [NS][Hv]
-  size_t dqk = 0;       // fp32 [NC*64][Hv][2][K]: per-v-head dq, dk before the group sum
   size_t total = 0;
 };
 
@@ -58,6 +57,7 @@ struct FwdArgs {
   const float *g, *h0;
   void *o;
   float *ht, *g_cum, *A, *h;
+  void *h_e;  // per-chunk states in the element type (backward's internal copy)
   char *ws;
   FwdWorkspace wl;
 };
@@ -77,6 +77,21 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 // states only (a.h), no output; T from Ain ([B,T,Hv,64] fp32) when given
 hipError_t launch_fwd_states(const FwdArgs &a, const float *Ain, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+
+// Benchmark timing: while enabled on the calling thread, each KernelTimer
+// scope records a HIP event before and after the kernel launched inside it,
+// on the launch stream (see gdn_timing_enable / gdn_timing_collect).
+class KernelTimer {
+ public:
+  KernelTimer(const char *name, hipStream_t stream);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer &) = delete;
+  KernelTimer &operator=(const KernelTimer &) = delete;
+
+ private:
+  int slot_;
+  hipStream_t stream_;
+};
 int run_selftest();
 
 }  // namespace gdn

@@ -269,6 +269,29 @@ __device__ __forceinline__ void tiles_store(const Tiles<Geo<E, K, V>::NTS> &s, f
   }
 }
 
+// Same as tiles_store for an element-type (bf16 or fp32) destination:
+// dst = tiles (+ dst if accumulate), rounded once to E.
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_store_e(const Tiles<Geo<E, K, V>::NTS> &s, E *dst,
+                                              bool accumulate) {
+  using G = Geo<E, K, V>;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  if (!G::owns(w)) return;
+  const int rt = G::srt(w);
+#pragma unroll
+  for (int m = 0; m < G::NTS; ++m) {
+    const int ct = G::sct(w) + m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = (16 * rt + 4 * lg + i) * V + 16 * ct + lr;
+      float x = s[m][i];
+      if (accumulate) x += to_f32(dst[off]);
+      dst[off] = from_f32<E>(x);
+    }
+  }
+}
+
 // Transposed working copy (element type) in LDS: dstT[v][i] = S[i][v].
 template <typename E, int K, int V>
 __device__ __forceinline__ void tiles_to_lds_t(const Tiles<Geo<E, K, V>::NTS> &s, E *dstT) {

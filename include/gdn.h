@@ -114,6 +114,18 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k,
  * problem (host-only planning query; 0 if invalid). */
 int64_t gdn_plan_segments(const gdn_problem_t *p);
 
+/* Kernel timing for benchmarks.  While enabled on the calling thread, every
+ * kernel the library enqueues is bracketed by a pair of HIP events recorded
+ * on the same stream (no host synchronisation).  gdn_timing_collect() waits
+ * for the recorded events, writes for each distinct kernel name (in first
+ * launch order, at most max_kernels): the name (NUL-terminated, 32 bytes per
+ * entry in `names`), the number of launches and their summed duration in
+ * milliseconds; it then forgets the record.  Returns the number of entries,
+ * or a negative error code.  Any output pointer may be NULL. */
+int gdn_timing_enable(int on); /* returns the previous setting */
+int gdn_timing_collect(int max_kernels, char *names, int32_t *counts,
+                       double *ms_total);
+
 /* Thread-local description of the last non-zero return ("" if none). */
 const char *gdn_last_error(void);
 
