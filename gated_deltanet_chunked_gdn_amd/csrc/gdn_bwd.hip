@@ -92,12 +92,12 @@ __device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem 
     }
   }
   if (tid < 64) {
-    const float gam = wave_incl_scan(pf.g);
+    const float gam = wave_incl_scan(pf.g) * kLog2e;
     const float gL = __shfl(gam, 63, 64);
-    const float eg = expf(gam);
+    const float eg = __builtin_amdgcn_exp2f(gam);
     S.gate.gam[tid] = gam;
     S.gate.eg[tid] = eg;
-    S.gate.dec[tid] = expf(gL - gam);
+    S.gate.dec[tid] = __builtin_amdgcn_exp2f(gL - gam);
     S.gate.bet[tid] = pf.b;
     S.wq[tid] = scale * eg;
     S.wk[tid] = -pf.b * eg;
@@ -195,7 +195,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * rt + 4 * lg + i;
-          pv[i] = (t <= s) ? qk[cc][i] * expf(S.gate.gam[s] - gt) : 0.f;
+          pv[i] = (t <= s) ? qk[cc][i] * __builtin_amdgcn_exp2f(S.gate.gam[s] - gt) : 0.f;
         }
         st4(sPt + t * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
       }

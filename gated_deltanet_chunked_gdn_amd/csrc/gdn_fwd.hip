@@ -58,17 +58,53 @@ __global__ void plan_kernel(Problem p, int seg_chunks, int32_t *chunk_prefix,
 
 // ------------------------------------------------------------------- prep
 // One workgroup per (chunk, q/k head); its waves take the group's v-heads.
-// K K^T is formed once on MFMA; per v-head: gate cumsum, the strictly lower
+// K K^T is formed once on MFMA.  Per v-head: gate cumsum, the strictly lower
 // A = beta_r exp(gamma_r - gamma_j) (k_r . k_j), and T = (I + A)^-1 by a
-// right-looking forward substitution with one lane per column of T (fp32).
+// blocked inversion on 16 x 16 blocks, all in fp32:
+//   diagonal blocks  T_bb = (I + A_bb)^-1  by forward substitution (one lane
+//                    per column, the four blocks side by side in one wave);
+//   off-diagonal     T_ij = -T_ii (sum_{j<=k<i} A_ik T_kj), level by level
+//                    (i - j = 1, 2, 3) as 16x16x16 fp32 MFMA products.
 template <typename E, int K>
 struct PrepCfg {
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = K + PAD;
-  static constexpr int LDA = 68;
+  static constexpr int LDA = 68;                          // fp32 64x64 rows
   static constexpr int bytesK = 64 * LDK * (int)sizeof(E);
-  static constexpr int bytesA = 64 * LDA * 4;  // per wave
+  // per wave, 16x16 fp32 blocks with row stride 17 (the MFMA operand reads
+  // of 16 rows x 4 columns then hit distinct banks): the 6 off-diagonal A
+  // blocks, the 10 lower blocks of T, one product; plus the 4 diagonal A
+  // blocks transposed with row stride 20 (float4 reads)
+  static constexpr int BS = 16 * 17;
+  static constexpr int fA = 0, fT = 6 * BS, fM = 16 * BS, fAd = 17 * BS;
+  static constexpr int floatsW = fAd + 4 * 16 * 20;
+  static constexpr int bytesW = floatsW * 4;
 };
+
+// acc += X * Y for 16x16 fp32 blocks stored row-major with stride ld
+__device__ __forceinline__ f32x4 mm16(f32x4 acc, const float *X, const float *Y, int ld) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[lr * ld + 4 * s + lg],
+                                               Y[(4 * s + lg) * ld + lr], acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 16x16 accumulator tile -> row-major block (stride ld), optionally negated
+__device__ __forceinline__ void put16(float *dst, int ld, f32x4 c, float sgn) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[(4 * lg + i) * ld + lr] = sgn * c[i];
+}
 
 template <typename E, int K>
 __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
@@ -120,8 +156,13 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
         for (int ct = 0; ct <= rt; ++ct, ++t) kk[t] = M::mma(x[rt], x[ct], kk[t]);
     }
   }
-  __syncthreads();  // the per-wave A buffers alias sK
-  float *sA = reinterpret_cast<float *>(smem) + w * (64 * C::LDA);
+  __syncthreads();  // the per-wave buffers alias sK
+  float *W = reinterpret_cast<float *>(smem) + w * C::floatsW;
+  float *sA = W + C::fA, *sT = W + C::fT, *sAd = W + C::fAd, *sM = W + C::fM;
+  constexpr int LD = 17, BS = C::BS;
+  // lower block (i >= j) of T, off-diagonal block (i > j) of A
+#define TB(i, j) (sT + (((i) * ((i) + 1)) / 2 + (j)) * BS)
+#define AB(i, j) (sA + (((i) * ((i) - 1)) / 2 + (j)) * BS)
   E *tmat = reinterpret_cast<E *>(a.ws + a.wl.tmat);
   for (int hl = w; hl < G; hl += nw) {
     const int h = hq * G + hl;
@@ -129,66 +170,106 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
     const float gv = lane < rows ? a.g[gi] : 0.f;
     const float bv = lane < rows ? to_f32(reinterpret_cast<const E *>(a.beta)[gi]) : 0.f;
     const float gam = wave_incl_scan(gv);
-    // A[r][j] (row-major, only the strictly lower tiles matter)
-    int t = 0;
+    const float gam2 = gam * kLog2e;
+    // A = strict_lower(beta_r exp(gamma_r - gamma_j) KK): off-diagonal blocks
+    // row-major, diagonal blocks transposed
+    {
+      int t = 0;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int ct = 0; ct <= rt; ++ct, ++t) {
-        const int j = 16 * ct + lr;
-        const float gj = __shfl(gam, j, 64);
+        for (int ct = 0; ct <= rt; ++ct, ++t) {
+          const int j = 16 * ct + lr;
+          const float gj = __shfl(gam2, j, 64);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * lg + i;
-          const float gr = __shfl(gam, r, 64);
-          const float br = __shfl(bv, r, 64);
-          float val = 0.f;
-          if (j < r) val = br * expf(gr - gj) * kk[t][i];
-          sA[r * C::LDA + j] = val;
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * lg + i;
+            const float gr = __shfl(gam2, r, 64);
+            const float br = __shfl(bv, r, 64);
+            const float val = (j < r) ? br * __builtin_amdgcn_exp2f(gr - gj) * kk[t][i] : 0.f;
+            if (ct == rt)
+              sAd[(rt * 16 + lr) * 20 + 4 * lg + i] = val;
+            else
+              AB(rt, ct)[(4 * lg + i) * LD + lr] = val;
+          }
+        }
+    }
+    wave_sync();
+    // diagonal blocks: lane = (block b, column c)
+    {
+      const int b = lane >> 4, c = lane & 15;
+      const float *at = sAd + b * 16 * 20;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        x[j] = (j == c ? 1.f : 0.f) - x[j];
+#pragma unroll
+        for (int r0 = (j + 1) & ~3; r0 < 16; r0 += 4) {
+          const float4 a4 = *reinterpret_cast<const float4 *>(at + j * 20 + r0);
+          if (r0 + 0 > j) x[r0 + 0] += a4.x * x[j];
+          if (r0 + 1 > j) x[r0 + 1] += a4.y * x[j];
+          if (r0 + 2 > j) x[r0 + 2] += a4.z * x[j];
+          if (r0 + 3 > j) x[r0 + 3] += a4.w * x[j];
         }
       }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // lane r keeps row r of A in registers (entries j < 16 * (r / 16 + 1))
-    float arow[64];
+      float *tb = sT + ((b * (b + 1)) / 2 + b) * BS;
 #pragma unroll
-    for (int q4 = 0; q4 < 16; ++q4) {
-      const float4 v4 = *reinterpret_cast<const float4 *>(sA + lane * C::LDA + 4 * q4);
-      arow[4 * q4 + 0] = v4.x;
-      arow[4 * q4 + 1] = v4.y;
-      arow[4 * q4 + 2] = v4.z;
-      arow[4 * q4 + 3] = v4.w;
+      for (int r = 0; r < 16; ++r) tb[r * LD + c] = x[r];
     }
-    // column `lane` of T:  x_r = delta_{r,lane} - sum_{j<r} A_rj x_j, formed
-    // right-looking: once x_j is final it is pushed into every later row.
-    // A_rj is wave-uniform: read from lane r's registers (v_readlane).
-    float x[64];
+    wave_sync();
+    // level 1: T_{b+1,b} = -T_{b+1,b+1} A_{b+1,b} T_bb
 #pragma unroll
-    for (int r = 0; r < 64; ++r) x[r] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      float acol[64];  // A[r][j] for r > j, wave-uniform (scalar registers)
-#pragma unroll
-      for (int r = j + 1; r < 64; ++r)
-        acol[r] = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, arow[j]), r));
-      x[j] = (j == lane ? 1.f : 0.f) - x[j];
-#pragma unroll
-      for (int r = j + 1; r < 64; ++r) x[r] += acol[r] * x[j];
+    for (int b = 0; b < 3; ++b) {
+      f32x4 m = mm16(zero4(), AB(b + 1, b), TB(b, b), LD);
+      put16(sM, LD, m, 1.f);
+      wave_sync();
+      f32x4 t1 = mm16(zero4(), TB(b + 1, b + 1), sM, LD);
+      wave_sync();
+      put16(TB(b + 1, b), LD, t1, -1.f);
     }
+    wave_sync();
+    // level 2: T_{b+2,b} = -T_{b+2,b+2} (A_{b+2,b} T_bb + A_{b+2,b+1} T_{b+1,b})
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x4 m = mm16(zero4(), AB(b + 2, b), TB(b, b), LD);
+      m = mm16(m, AB(b + 2, b + 1), TB(b + 1, b), LD);
+      put16(sM, LD, m, 1.f);
+      wave_sync();
+      f32x4 t2 = mm16(zero4(), TB(b + 2, b + 2), sM, LD);
+      wave_sync();
+      put16(TB(b + 2, b), LD, t2, -1.f);
+    }
+    wave_sync();
+    // level 3: T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
+    {
+      f32x4 m = mm16(zero4(), AB(3, 0), TB(0, 0), LD);
+      m = mm16(m, AB(3, 1), TB(1, 0), LD);
+      m = mm16(m, AB(3, 2), TB(2, 0), LD);
+      put16(sM, LD, m, 1.f);
+      wave_sync();
+      f32x4 t3 = mm16(zero4(), TB(3, 3), sM, LD);
+      put16(TB(3, 0), LD, t3, -1.f);
+    }
+    wave_sync();
+    // T out, lane = column: element type (internal, chunk-contiguous rows)
+    // and fp32 A (rows at their tokens)
     E *tm = tmat + (gid * p.Hv + h) * 64 * 64;
+    const int cb = lane >> 4, cc = lane & 15;
 #pragma unroll
-    for (int r = 0; r < 64; ++r) tm[r * 64 + lane] = from_f32<E>(x[r]);
-    if (a.A) {
-#pragma unroll
-      for (int r = 0; r < 64; ++r)
-        if (r < rows) a.A[((tok0 + r) * p.Hv + h) * 64 + lane] = x[r];
+    for (int r = 0; r < 64; ++r) {
+      const int rb = r >> 4;
+      const float x = (cb > rb) ? 0.f
+                                : sT[(((rb * (rb + 1)) / 2) + cb) * BS + (r & 15) * LD + cc];
+      tm[r * 64 + lane] = from_f32<E>(x);
+      if (a.A && r < rows) a.A[((tok0 + r) * p.Hv + h) * 64 + lane] = x;
     }
     if (a.g_cum && lane < rows) a.g_cum[gi] = gam;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    wave_sync();
   }
+#undef TB
+#undef AB
 }
 
 // T from a caller-supplied A ([B,T,Hv,64] fp32, chunk rows at their tokens);
@@ -336,13 +417,9 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       tiles_store_e<E, K, V>(st, hs, MODE == kFix);
     }
     // ---- phase A: Q S, K S (this wave's row tile, its half of V), Q K^T
-    typename M::frag qa[NKK], ka[NKK];
-#pragma unroll
-    for (int ks = 0; ks < NKK; ++ks) {
-      qa[ks] = M::ld(sQ + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
-      ka[ks] = M::ld(sK + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
-    }
+    const int pc0 = 2 * (w >> 2);  // P column tiles of this wave: pc0, pc0 + 1
     f32x4 qs[NCH], kss[NCH];
+    f32x4 qk[2] = {zero4(), zero4()};
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) {
       qs[c2] = zero4();
@@ -350,11 +427,20 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
     }
 #pragma unroll
     for (int ks = 0; ks < NKK; ++ks) {
+      const auto qa = M::ld(sQ + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
+      const auto ka = M::ld(sK + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
 #pragma unroll
       for (int c2 = 0; c2 < NCH; ++c2) {
         const auto b = M::ld(sSt + (16 * (ct0 + c2) + lr) * G::LDK + ks * KS + EPL * lg);
-        if (WRITE_O) qs[c2] = M::mma(qa[ks], b, qs[c2]);
-        kss[c2] = M::mma(ka[ks], b, kss[c2]);
+        if (WRITE_O) qs[c2] = M::mma(qa, b, qs[c2]);
+        kss[c2] = M::mma(ka, b, kss[c2]);
+      }
+      if (WRITE_O) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+          if (pc0 + cc <= rt)
+            qk[cc] = M::mma(
+                qa, M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg), qk[cc]);
       }
     }
     float eg_r[4], b_r[4];
@@ -365,17 +451,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       b_r[i] = S.gate.bet[r];
     }
     if (WRITE_O) {
-      // P = lower_incl(Q K^T * E): this wave does column tiles 2*(w>>2) + {0,1}
-      const int pc0 = 2 * (w >> 2);
-      f32x4 qk[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int ks = 0; ks < NKK; ++ks)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          if (pc0 + cc <= rt)
-            qk[cc] = M::mma(
-                qa[ks], M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg),
-                qk[cc]);
+      // P = lower_incl(Q K^T * E): this wave does column tiles pc0, pc0 + 1
       float gam_r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) gam_r[i] = S.gate.gam[16 * rt + 4 * lg + i];
@@ -386,7 +462,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * lg + i;
-          const float val = (j <= r) ? qk[cc][i] * expf(gam_r[i] - gj) : 0.f;
+          const float val = (j <= r) ? qk[cc][i] * __builtin_amdgcn_exp2f(gam_r[i] - gj) : 0.f;
           sP[r * G::LDC + j] = from_f32<E>(val);
         }
       }
@@ -623,8 +699,8 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
   }
   using C = PrepCfg<E, K>;
   const int G = p.Hv / p.Hq;
-  const int nw = G < 4 ? G : 4;
-  const size_t lds = (size_t)(C::bytesK > nw * C::bytesA ? C::bytesK : nw * C::bytesA);
+  const int nw = G < 2 ? G : 2;
+  const size_t lds = (size_t)(C::bytesK > nw * C::bytesW ? C::bytesK : nw * C::bytesW);
   KernelTimer kt("prep", st);
   prep_kernel<E, K><<<dim3((unsigned)(pl.total_chunks * p.Hq)), 64 * nw, lds, st>>>(a);
 }

@@ -10,6 +10,7 @@
 namespace gdn {
 
 constexpr int kNW = 8;              // waves per segment workgroup
+constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 64 * kNW;  // 512
 
 struct SeqInfo {
@@ -199,7 +200,7 @@ __device__ __forceinline__ void pref_load(Pref<E, K, V> &pf, const Problem &p, c
 
 // Per-chunk gate quantities in LDS.
 struct GateLds {
-  float *gam;  // inclusive cumsum gamma_r
+  float *gam;  // inclusive cumsum gamma_r, times log2(e) (decays are exp2 of differences)
   float *eg;   // exp(gamma_r)
   float *dec;  // exp(gamma_L - gamma_r)
   float *bet;  // beta_r
@@ -209,11 +210,11 @@ struct GateLds {
 __device__ __forceinline__ void gate_commit(float g, float b, const GateLds &G) {
   const int tid = threadIdx.x;
   if (tid < 64) {
-    const float gam = wave_incl_scan(g);
+    const float gam = wave_incl_scan(g) * kLog2e;
     const float gL = __shfl(gam, 63, 64);
     G.gam[tid] = gam;
-    G.eg[tid] = expf(gam);
-    G.dec[tid] = expf(gL - gam);
+    G.eg[tid] = __builtin_amdgcn_exp2f(gam);
+    G.dec[tid] = __builtin_amdgcn_exp2f(gL - gam);
     G.bet[tid] = b;
   }
 }
