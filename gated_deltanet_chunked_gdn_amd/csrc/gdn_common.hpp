@@ -43,26 +43,38 @@ struct Mma<bf16> {
   __device__ static __forceinline__ frag ld(const bf16 *p) {
     return *reinterpret_cast<const frag *>(p);
   }
-  // 8 elements at stride `stride` (element units), each scaled by w[e]
-  __device__ static __forceinline__ frag ld_strided_scaled(const bf16 *p, int stride,
-                                                  const float *w) {
+  // Operand fragment of a matrix stored k-major in LDS (X[k][c], contiguous
+  // along c, row pitch `ld` elements, ld % 4 == 0): `tile` = &X[k0][c0] with
+  // c0 % 4 == 0.  Lane l receives X[k0 + 8*(l >> 4) + e][c0 + (l & 15)] for
+  // e < 8, from two LDS transpose reads (ds_read_b64_tr_b16).  That
+  // instruction works on groups of 16 lanes: each lane reads 4 contiguous
+  // 16-bit elements, and output lane j receives element j & 3 of the group's
+  // lanes 4e + (j >> 2), e < 4.  Source lane s of a group therefore points at
+  // row (s >> 2) and columns 4*(s & 3) .. +3 of a 4 x 16 block.
+  __device__ static __forceinline__ frag ld_tr(const bf16 *tile, int ld) {
+    const int l = threadIdx.x & 63;
+    const bf16 *p = tile + (8 * (l >> 4) + ((l & 15) >> 2)) * ld + 4 * (l & 3);
+    typedef __attribute__((address_space(3))) bf16x4 lds4;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4 *)p);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4 *)(p + 4 * ld));
+    return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  // ld_tr with element e scaled by w[8*(l >> 4) + e] (a factor per row k)
+  __device__ static __forceinline__ frag ld_tr_scaled(const bf16 *tile, int ld, const float *w) {
+    const frag x = ld_tr(tile, ld);
+    const float *wl = w + 8 * ((threadIdx.x & 63) >> 4);
     frag f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)p[e * stride] * w[e]);
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)x[e] * wl[e]);
     return f;
   }
-  // 8 elements at stride `stride`
-  __device__ static __forceinline__ frag ld_strided(const bf16 *p, int stride) {
+  // X[m][k] + X[k][m]: 8 contiguous elements at p (as ld) plus the k-major
+  // fragment of the same tile (rounded once)
+  __device__ static __forceinline__ frag ld_sym_tr(const bf16 *p, const bf16 *tile, int pitch) {
+    const frag a = ld(p), b = ld_tr(tile, pitch);
     frag f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = p[e * stride];
-    return f;
-  }
-  // 8 contiguous elements of p plus 8 strided elements of q (sum, rounded)
-  __device__ static __forceinline__ frag ld_sym(const bf16 *p, const bf16 *q, int stride) {
-    frag f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)p[e] + (float)q[e * stride]);
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)a[e] + (float)b[e]);
     return f;
   }
 };
@@ -76,13 +88,16 @@ struct Mma<float> {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ frag ld(const float *p) { return *p; }
-  __device__ static __forceinline__ frag ld_strided_scaled(const float *p, int stride,
-                                                  const float *w) {
-    return p[0] * w[0];
+  // k-major operand (see Mma<bf16>::ld_tr): lane l reads X[k0 + (l >> 4)][c0 + (l & 15)]
+  __device__ static __forceinline__ frag ld_tr(const float *tile, int ld) {
+    const int l = threadIdx.x & 63;
+    return tile[(l >> 4) * ld + (l & 15)];
   }
-  __device__ static __forceinline__ frag ld_strided(const float *p, int stride) { return p[0]; }
-  __device__ static __forceinline__ frag ld_sym(const float *p, const float *q, int stride) {
-    return p[0] + q[0];
+  __device__ static __forceinline__ frag ld_tr_scaled(const float *tile, int ld, const float *w) {
+    return ld_tr(tile, ld) * w[(threadIdx.x & 63) >> 4];
+  }
+  __device__ static __forceinline__ frag ld_sym_tr(const float *p, const float *tile, int ld) {
+    return p[0] + ld_tr(tile, ld);
   }
 };
 

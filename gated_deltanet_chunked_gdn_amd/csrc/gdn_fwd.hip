@@ -544,9 +544,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       typename M::frag kt[NKC];
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks) {
-        const int t0 = ks * KS + EPL * lg;
-        kt[ks] = M::ld_strided_scaled(sK + t0 * G::LDK + 16 * srt + lr, G::LDK,
-                                      S.gate.dec + t0);
+        kt[ks] = M::ld_tr_scaled(sK + ks * KS * G::LDK + 16 * srt, G::LDK, S.gate.dec + ks * KS);
       }
 #pragma unroll
       for (int m = 0; m < G::NTS; ++m)
