@@ -272,14 +272,13 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
         for (int i = 0; i < 4; ++i) st[m][i] *= egL;
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks) {
-        const int t0 = ks * KS + EPL * lg;
-        const auto kt = M::ld_strided(sK + t0 * G::LDK + 16 * srt + lr, G::LDK);
+        const auto kt = M::ld_tr(sK + ks * KS * G::LDK + 16 * srt, G::LDK);
 #pragma unroll
         for (int m = 0; m < G::NTS; ++m)
           st[m] = M::mma(kt, M::ld(sXt + (16 * (sct + m) + lr) * G::LDC + ks * KS + EPL * lg),
                          st[m]);
         if (MAIN) {
-          const auto qt = M::ld_strided_scaled(sQ + t0 * G::LDK + 16 * srt + lr, G::LDK, S.wq + t0);
+          const auto qt = M::ld_tr_scaled(sQ + ks * KS * G::LDK + 16 * srt, G::LDK, S.wq + ks * KS);
 #pragma unroll
           for (int m = 0; m < G::NTS; ++m)
             st[m] = M::mma(qt,
@@ -416,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
 template <typename E, int K, int V>
 struct LocCfg {
   using G = Geo<E, K, V>;
-  static constexpr int VB = (sizeof(E) == 4) ? (V < 32 ? V : 32) : (V < 64 ? V : 64);
+  static constexpr int VB = 32;
   static constexpr int NVB = V / VB;
   static constexpr int LDB = VB + G::PAD;
   static constexpr int NCHB = VB / 32;  // V-block column tiles per half
@@ -432,7 +431,8 @@ struct LocCfg {
   static constexpr int oVn = oRt + VB * G::LDC;    // Vn [64][LDB]
   static constexpr int oPE = oVn + 64 * LDB;       // dP * E [64][LDC]
   static constexpr int oKK = oPE + 64 * G::LDC;    // dKK [64][LDC]
-  static constexpr int nE = oKK + 64 * G::LDC;
+  static constexpr int oV = oKK + 64 * G::LDC;     // V block [64][LDB]
+  static constexpr int nE = oV + 64 * LDB;
   static constexpr int bytes = nE * (int)sizeof(E);
 };
 
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   constexpr int NKB = C::VB / KS;
   constexpr int VB = C::VB, LDB = C::LDB, NCHB = C::NCHB, NCHK = C::NCHK;
   __shared__ __attribute__((aligned(16))) char smem_[C::bytes];
-  __shared__ float sgam[64], seg[64], sdec[64], sbet[64];
+  __shared__ __attribute__((aligned(16))) float sgam[64], seg[64], sdec[64], sbet[64];
   __shared__ float rowp[4][2][64];  // [de, db, rs, c][half][row]
   __shared__ float colp[4][64];     // [row tile][col]
   __shared__ float glp[kNW];
@@ -484,6 +484,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   E *sVn = sm + C::oVn;
   E *sPE = sm + C::oPE;
   E *sKK = sm + C::oKK;
+  E *sV = sm + C::oV;
 
   const Problem &p = a.p;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -513,6 +514,16 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   E *dvp = reinterpret_cast<E *>(a.dv);
   E *dbp = reinterpret_cast<E *>(a.dbeta);
   constexpr int VEC = G::VEC;
+  // Per-workgroup tile bases (uniform, held in scalar registers) and 32-bit
+  // byte offsets per lane: row strides of q/k and of v/do/dv in bytes.
+  const uint32_t qk_rs = (uint32_t)(p.Hq * K * sizeof(E));
+  const uint32_t v_rs = (uint32_t)(p.Hv * V * sizeof(E));
+  const char *qtile = reinterpret_cast<const char *>(qp + (tok0 * p.Hq + hq) * K);
+  const char *ktile = reinterpret_cast<const char *>(kp + (tok0 * p.Hq + hq) * K);
+  // 4 per-row values of this lane's accumulator rows 16 rt + 4 lg + i
+  auto row4 = [&](const float *arr) {
+    return *reinterpret_cast<const f32x4 *>(arr + 16 * rt + 4 * lg);
+  };
 
   // ---- chunk tiles of q and k (shared by the group's v-heads)
   {
@@ -521,9 +532,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       const int r = idx / PK, cv = idx % PK;
       uint4 zq = make_uint4(0u, 0u, 0u, 0u), zk = zq;
       if (r < rows) {
-        const int64_t off = ((tok0 + r) * p.Hq + hq) * K + cv * VEC;
-        zq = *reinterpret_cast<const uint4 *>(qp + off);
-        zk = *reinterpret_cast<const uint4 *>(kp + off);
+        const uint32_t off = r * qk_rs + cv * 16u;
+        zq = *reinterpret_cast<const uint4 *>(qtile + off);
+        zk = *reinterpret_cast<const uint4 *>(ktile + off);
       }
       *reinterpret_cast<uint4 *>(sQ + r * G::LDK + cv * VEC) = zq;
       *reinterpret_cast<uint4 *>(sK + r * G::LDK + cv * VEC) = zk;
@@ -532,24 +543,26 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   __syncthreads();
 #define QA(ks) M::ld(sQ + ra * G::LDK + (ks) * KS + EPL * lg)
 #define KA(ks) M::ld(sK + ra * G::LDK + (ks) * KS + EPL * lg)
-  // raw Q K^T and K K^T tiles of this wave (fp32, shared by the v-heads)
-  f32x4 qk[2], kk[2];
+  // raw Q K^T and (if wanted) K K^T tiles of this wave (fp32); recomputed
+  // where needed rather than held across the v-block loop
+  auto qk_tiles = [&](f32x4 *qk, f32x4 *kk) {
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
-    qk[cc] = zero4();
-    kk[cc] = zero4();
-  }
+    for (int cc = 0; cc < 2; ++cc) {
+      qk[cc] = zero4();
+      if (kk) kk[cc] = zero4();
+    }
 #pragma unroll
-  for (int ks = 0; ks < NKK; ++ks) {
-    const auto qa = QA(ks), ka = KA(ks);
+    for (int ks = 0; ks < NKK; ++ks) {
+      const auto qa = QA(ks);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-      if (pc0 + cc <= rt) {
-        const auto kb = M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg);
-        qk[cc] = M::mma(qa, kb, qk[cc]);
-        kk[cc] = M::mma(ka, kb, kk[cc]);
-      }
-  }
+      for (int cc = 0; cc < 2; ++cc)
+        if (pc0 + cc <= rt) {
+          const auto kb = M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg);
+          qk[cc] = M::mma(qa, kb, qk[cc]);
+          if (kk) kk[cc] = M::mma(KA(ks), kb, kk[cc]);
+        }
+    }
+  };
   // dq, dk of the q/k head: every term is accumulated in place
   f32x4 dq[NCHK], dk[NCHK];
 #pragma unroll
@@ -583,20 +596,18 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    float gam_s[4], eg_s[4], dec_s[4], bet_s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = 16 * rt + 4 * lg + i;
-      gam_s[i] = sgam[s];
-      eg_s[i] = seg[s];
-      dec_s[i] = sdec[s];
-      bet_s[i] = sbet[s];
-    }
+    const char *vtile = reinterpret_cast<const char *>(vp + (tok0 * p.Hv + h) * V);
+    const char *dotile = reinterpret_cast<const char *>(dop + (tok0 * p.Hv + h) * V);
+    char *dvtile = reinterpret_cast<char *>(dvp + (tok0 * p.Hv + h) * V);
     // row factors of this lane's A-operand row
     const float f_q = scale * seg[ra];            // dq  += (scale e^g dO) S^T
     const float f_r = -sbet[ra] * seg[ra];        // dk  += (-beta e^g dR) S^T
     const float f_v = sdec[ra];                   // dk  += (e^{gL-g} Vn) D^T
     // P^T (P = lower_incl(Q K^T * E)) of this v-head into LDS
+    {
+    f32x4 qk[2];
+    qk_tiles(qk, nullptr);
+    const f32x4 gam_s = row4(sgam);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const int t = 16 * (pc0 + cc) + lr;
@@ -608,6 +619,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         pv[i] = (t <= s) ? qk[cc][i] * expf(gam_s[i] - gt) : 0.f;
       }
       st4(sPt + t * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
+    }
     }
     f32x4 dp[2], da[2];
 #pragma unroll
@@ -640,22 +652,16 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         }
         for (int idx = tid; idx < 64 * PB; idx += kThreads) {
           const int r = idx / PB, cv = idx % PB;
-          uint4 z = make_uint4(0u, 0u, 0u, 0u);
-          if (r < rows)
-            z = *reinterpret_cast<const uint4 *>(dop + ((tok0 + r) * p.Hv + h) * V + v0 +
-                                                 cv * VEC);
+          uint4 z = make_uint4(0u, 0u, 0u, 0u), zv = z;
+          if (r < rows) {
+            const uint32_t off = r * v_rs + (uint32_t)((v0 + cv * VEC) * sizeof(E));
+            z = *reinterpret_cast<const uint4 *>(dotile + off);
+            zv = *reinterpret_cast<const uint4 *>(vtile + off);
+          }
           *reinterpret_cast<uint4 *>(sDO + r * LDB + cv * VEC) = z;
+          *reinterpret_cast<uint4 *>(sV + r * LDB + cv * VEC) = zv;
         }
       }
-      float vv[NCHB][4];
-#pragma unroll
-      for (int m = 0; m < NCHB; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * rt + 4 * lg + i;
-          const int vc = 16 * (ch * NCHB + m) + lr;
-          vv[m][i] = s < rows ? to_f32(vp[((tok0 + s) * p.Hv + h) * V + v0 + vc]) : 0.f;
-        }
       __syncthreads();
       // ---- phase 2: K S, Q S; R; dq += (scale e^g dO) S^T
       f32x4 ks_[NCHB], qs_[NCHB];
@@ -670,12 +676,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < NCHB; ++m) {
           const auto b =
-              M::ld_strided(sS + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB);
+              M::ld_tr(sS + ks * KS * LDB + 16 * (ch * NCHB + m), LDB);
           ks_[m] = M::mma(ka, b, ks_[m]);
           qs_[m] = M::mma(qa, b, qs_[m]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      {
+      const f32x4 bet_s = row4(sbet), eg_s = row4(seg);
 #pragma unroll
       for (int m = 0; m < NCHB; ++m) {
         const int vc = 16 * (ch * NCHB + m) + lr;
@@ -683,10 +691,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * rt + 4 * lg + i;
-          rr[i] = bet_s[i] * (vv[m][i] - eg_s[i] * ks_[m][i]);
+          rr[i] = bet_s[i] * (to_f32(sV[s * LDB + vc]) - eg_s[i] * ks_[m][i]);
           de_p[i] += scale * to_f32(sDO[s * LDB + vc]) * qs_[m][i];
         }
         st4(sRt + vc * G::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
+      }
       }
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
@@ -720,11 +729,12 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
             kd[m] = M::mma(
-                ka, M::ld_strided(sD + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB),
+                ka, M::ld_tr(sD + ks * KS * LDB + 16 * (ch * NCHB + m), LDB),
                 kd[m]);
           __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();  // R^T fully consumed before dVn^T overwrites it
+        const f32x4 dec_s = row4(sdec);
 #pragma unroll
         for (int m = 0; m < NCHB; ++m) {
           const int vc = 16 * (ch * NCHB + m) + lr;
@@ -744,7 +754,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
             x[m] = M::mma(
-                pa, M::ld_strided(sDO + (ks * KS + EPL * lg) * LDB + 16 * (ch * NCHB + m) + lr, LDB),
+                pa, M::ld_tr(sDO + ks * KS * LDB + 16 * (ch * NCHB + m), LDB),
                 x[m]);
         }
 #pragma unroll
@@ -771,7 +781,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       for (int m = 0; m < NCHB; ++m) dr[m] = zero4();
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks) {
-        const auto tta = M::ld_strided(sT + (ks * KS + EPL * lg) * G::LDC + 16 * rt + lr, G::LDC);
+        const auto tta = M::ld_tr(sT + ks * KS * G::LDC + 16 * rt, G::LDC);
 #pragma unroll
         for (int m = 0; m < NCHB; ++m)
           dr[m] = M::mma(
@@ -779,6 +789,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
               dr[m]);
       }
       __syncthreads();  // D block fully consumed before dR overwrites it
+      {
+      const f32x4 bet_s = row4(sbet), eg_s = row4(seg);
 #pragma unroll
       for (int m = 0; m < NCHB; ++m) {
         const int vc = 16 * (ch * NCHB + m) + lr;
@@ -787,10 +799,13 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           const int s = 16 * rt + 4 * lg + i;
           const float x = dr[m][i];
           sDR[s * LDB + vc] = from_f32<E>(x);
-          if (s < rows) dvp[((tok0 + s) * p.Hv + h) * V + v0 + vc] = from_f32<E>(bet_s[i] * x);
-          db_p[i] += x * (vv[m][i] - eg_s[i] * ks_[m][i]);
+          if (s < rows)
+            *reinterpret_cast<E *>(dvtile + s * v_rs + (uint32_t)((v0 + vc) * sizeof(E))) =
+                from_f32<E>(bet_s[i] * x);
+          db_p[i] += x * (to_f32(sV[s * LDB + vc]) - eg_s[i] * ks_[m][i]);
           de_p[i] -= bet_s[i] * x * ks_[m][i];
         }
+      }
       }
       __syncthreads();
       // ---- phase 6: dP += dO Vn^T, dA -= dR Vn^T, dk += (-beta e^g dR) S^T
@@ -814,6 +829,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     }
     // ---- phase 7: masks, dP*E, dKK, dgamma row/column terms
     float rs_p[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 qk[2], kk[2];
+    qk_tiles(qk, kk);
+    const f32x4 gam_s = row4(sgam), bet_s = row4(sbet);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const int t = 16 * (pc0 + cc) + lr;
@@ -865,16 +883,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     // ---- phase 8: dq += (dP*E) K;  dk += (dP*E)^T Q + (dKK + dKK^T) K
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
-      const int t0 = ks * KS + EPL * lg;
       const auto pea = M::ld(sPE + ra * G::LDC + ks * KS + EPL * lg);
-      const auto peta = M::ld_strided(sPE + t0 * G::LDC + 16 * rt + lr, G::LDC);
-      const auto ma = M::ld_sym(sKK + ra * G::LDC + ks * KS + EPL * lg,
-                                sKK + t0 * G::LDC + 16 * rt + lr, G::LDC);
+      const auto peta = M::ld_tr(sPE + ks * KS * G::LDC + 16 * rt, G::LDC);
+      const auto ma = M::ld_sym_tr(sKK + ra * G::LDC + ks * KS + EPL * lg,
+                                   sKK + ks * KS * G::LDC + 16 * rt, G::LDC);
 #pragma unroll
       for (int m = 0; m < NCHK; ++m) {
-        const int ic = 16 * (ch * NCHK + m) + lr;
-        const auto kb = M::ld_strided(sK + t0 * G::LDK + ic, G::LDK);
-        const auto qb = M::ld_strided(sQ + t0 * G::LDK + ic, G::LDK);
+        const auto kb = M::ld_tr(sK + ks * KS * G::LDK + 16 * (ch * NCHK + m), G::LDK);
+        const auto qb = M::ld_tr(sQ + ks * KS * G::LDK + 16 * (ch * NCHK + m), G::LDK);
         dq[m] = M::mma(pea, kb, dq[m]);
         dk[m] = M::mma(peta, qb, dk[m]);
         dk[m] = M::mma(ma, kb, dk[m]);
