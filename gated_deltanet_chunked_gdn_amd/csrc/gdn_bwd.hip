@@ -35,10 +35,10 @@ struct RevLds {
   using G = Geo<E, K, V>;
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + 64 * G::LDK;
-  static constexpr int oDOt = oK + 64 * G::LDK;   // dO^T [V][64]
-  static constexpr int oDt = oDOt + V * G::LDC;   // D^T  [V][K]
-  static constexpr int oTt = oDt + V * G::LDK;    // T^T  [64][64]
-  static constexpr int oPt = oTt + 64 * G::LDC;   // P^T  [64][64]
+  static constexpr int oDO = oK + 64 * G::LDK;    // dO   [64][V]
+  static constexpr int oDt = oDO + 64 * G::LDV;   // D^T  [V][K]
+  static constexpr int oT = oDt + V * G::LDK;     // T    [64][64]
+  static constexpr int oPt = oT + 64 * G::LDC;    // P^T  [64][64]
   static constexpr int oDVnt = oPt + 64 * G::LDC; // dVn^T [V][64]
   static constexpr int oXt = oDVnt + V * G::LDC;  // (-beta e^gamma T^T dVn)^T [V][64]
   static constexpr int nE = oXt + V * G::LDC;
@@ -54,11 +54,11 @@ struct RSmem {
 };
 
 template <typename E, int K, int V, bool MAIN>
-__device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem &S, float scale) {
+__device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem &S, float scale,
+                                           int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
   using L = RevLds<E, K, V>;
   E *sm = reinterpret_cast<E *>(S.base);
-  const int tid = threadIdx.x;
   constexpr int PK = K / G::VEC, PVr = V / G::VEC, PTr = 64 / G::VEC;
 #pragma unroll
   for (int m = 0; m < G::NQ; ++m) {
@@ -69,15 +69,15 @@ __device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem 
       *reinterpret_cast<uint4 *>(sm + L::oK + r * G::LDK + cv * G::VEC) = pf.k[m];
     }
   }
+  // dO and T stay row-major; their transposed operands come from LDS
+  // transpose reads
   if (MAIN) {
 #pragma unroll
     for (int m = 0; m < G::NV; ++m) {
       const int idx = tid + kThreads * m;
       if (idx < G::PV) {
         const int r = idx / PVr, cv = idx % PVr;
-        const E *e8 = reinterpret_cast<const E *>(&pf.v[m]);
-#pragma unroll
-        for (int e = 0; e < G::VEC; ++e) sm[L::oDOt + (cv * G::VEC + e) * G::LDC + r] = e8[e];
+        *reinterpret_cast<uint4 *>(sm + L::oDO + r * G::LDV + cv * G::VEC) = pf.v[m];
       }
     }
   }
@@ -86,9 +86,7 @@ __device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem 
     const int idx = tid + kThreads * m;
     if (idx < G::PT) {
       const int r = idx / PTr, cv = idx % PTr;
-      const E *e8 = reinterpret_cast<const E *>(&pf.t[m]);
-#pragma unroll
-      for (int e = 0; e < G::VEC; ++e) sm[L::oTt + (cv * G::VEC + e) * G::LDC + r] = e8[e];
+      *reinterpret_cast<uint4 *>(sm + L::oT + r * G::LDC + cv * G::VEC) = pf.t[m];
     }
   }
   if (tid < 64) {
@@ -98,9 +96,9 @@ __device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem 
     S.gate.gam[tid] = gam;
     S.gate.eg[tid] = eg;
     S.gate.dec[tid] = __builtin_amdgcn_exp2f(gL - gam);
-    S.gate.bet[tid] = pf.b;
+    S.gate.bet[tid] = pf.beta();
     S.wq[tid] = scale * eg;
-    S.wk[tid] = -pf.b * eg;
+    S.wk[tid] = -pf.beta() * eg;
   }
 }
 
@@ -125,14 +123,13 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
   E *sm = reinterpret_cast<E *>(S.base);
   const E *sQ = sm + L::oQ;
   const E *sK = sm + L::oK;
-  const E *sDOt = sm + L::oDOt;
+  const E *sDO = sm + L::oDO;
   E *sDt = sm + L::oDt;
-  const E *sTt = sm + L::oTt;
+  const E *sT = sm + L::oT;
   E *sPt = sm + L::oPt;
   E *sDVnt = sm + L::oDVnt;
   E *sXt = sm + L::oXt;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int w = wave_of(threadIdx.x);
   const int rt = w & 3;
   const int ct0 = (w >> 2) * NCH;
   const float scale = p.scale;
@@ -156,9 +153,18 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
   __syncthreads();
   bool zero_exit = false;
   for (int c = c_end - 1; c >= c_begin && !zero_exit; --c) {
+    const int tid = opaque_tid(), lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
     {
       E *ds = dstates + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
-      tiles_store_e<E, K, V>(st, ds, MODE == kRFix);
+      tiles_store_e<E, K, V>(st, ds, MODE == kRFix, tid);
+    }
+    // the previous chunk's inputs travel while this whole chunk is computed
+    if (c - 1 >= c_begin) {
+      const int c1 = c - 1;
+      pref_load<E, K, V, MAIN>(pf, p, qp, kp, dop, tmat, a.g, bp,
+                               si.tok0 + (int64_t)c1 * kChunk,
+                               min(kChunk, si.len - c1 * kChunk), h, chunk_gid0 + c1, tid);
     }
     // ---- phase A: K D (rows of tile rt, half of V); P^T
     typename M::frag ka[NKK];
@@ -201,12 +207,6 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
       }
     }
     __syncthreads();
-    if (c - 1 >= c_begin) {
-      const int c1 = c - 1;
-      pref_load<E, K, V, MAIN>(pf, p, qp, kp, dop, tmat, a.g, bp,
-                               si.tok0 + (int64_t)c1 * kChunk,
-                               min(kChunk, si.len - c1 * kChunk), h, chunk_gid0 + c1);
-    }
     // ---- phase B: dVn = dec * (K D) + scale P^T dO
     {
       float dec_r[4];
@@ -225,7 +225,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
 #pragma unroll
           for (int c2 = 0; c2 < NCH; ++c2)
             x[c2] = M::mma(
-                pa[ks], M::ld(sDOt + (16 * (ct0 + c2) + lr) * G::LDC + ks * KS + EPL * lg),
+                pa[ks], M::ld_tr(sDO + ks * KS * G::LDV + 16 * (ct0 + c2), G::LDV, lane),
                 x[c2]);
       }
 #pragma unroll
@@ -242,7 +242,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
       typename M::frag ta[NKC];
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks)
-        ta[ks] = M::ld(sTt + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+        ta[ks] = M::ld_tr(sT + ks * KS * G::LDC + 16 * rt, G::LDC, lane);
       f32x4 x[NCH];
 #pragma unroll
       for (int c2 = 0; c2 < NCH; ++c2) x[c2] = zero4();
@@ -272,29 +272,29 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
         for (int i = 0; i < 4; ++i) st[m][i] *= egL;
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks) {
-        const auto kt = M::ld_tr(sK + ks * KS * G::LDK + 16 * srt, G::LDK);
+        const auto kt = M::ld_tr(sK + ks * KS * G::LDK + 16 * srt, G::LDK, lane);
 #pragma unroll
         for (int m = 0; m < G::NTS; ++m)
           st[m] = M::mma(kt, M::ld(sXt + (16 * (sct + m) + lr) * G::LDC + ks * KS + EPL * lg),
                          st[m]);
         if (MAIN) {
-          const auto qt = M::ld_tr_scaled(sQ + ks * KS * G::LDK + 16 * srt, G::LDK, S.wq + ks * KS);
+          const auto qt =
+              M::ld_tr_scaled(sQ + ks * KS * G::LDK + 16 * srt, G::LDK, S.wq + ks * KS, lane);
 #pragma unroll
           for (int m = 0; m < G::NTS; ++m)
-            st[m] = M::mma(qt,
-                           M::ld(sDOt + (16 * (sct + m) + lr) * G::LDC + ks * KS + EPL * lg),
+            st[m] = M::mma(qt, M::ld_tr(sDO + ks * KS * G::LDV + 16 * (sct + m), G::LDV, lane),
                            st[m]);
         }
       }
     }
-    tiles_to_lds_t<E, K, V>(st, sDt);
+    tiles_to_lds_t<E, K, V>(st, sDt, tid);
     if (MODE == kRFix) {
       zero_exit = !block_any(tiles_nonzero<E, K, V>(st), S.flag);
     } else {
       __syncthreads();
     }
     if (c - 1 >= c_begin && !zero_exit) {
-      rev_commit<E, K, V, MAIN>(pf, S, scale);
+      rev_commit<E, K, V, MAIN>(pf, S, scale, tid);
       __syncthreads();
     }
   }
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
 template <typename E, int K, int V>
 struct LocCfg {
   using G = Geo<E, K, V>;
-  static constexpr int VB = 32;
+  static constexpr int VB = (sizeof(E) == 4) ? 32 : (V < 64 ? V : 64);
   static constexpr int NVB = V / VB;
   static constexpr int LDB = VB + G::PAD;
   static constexpr int NCHB = VB / 32;  // V-block column tiles per half
@@ -436,12 +436,19 @@ struct LocCfg {
   static constexpr int bytes = nE * (int)sizeof(E);
 };
 
-// 16-lane (same lane group) sum over the 16 column lanes
+// x moved across lanes by a DPP control (rows of 16 lanes)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of each DPP row (the lanes that share l >> 4): swap
+// neighbours and pairs inside quads, then rotate the row by 4 and by 8.
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x124>(x);  // row_ror:4
+  x += dpp<0x128>(x);  // row_ror:8
   return x;
 }
 
@@ -455,6 +462,18 @@ __device__ __forceinline__ bf16x8 frag_scale(bf16x8 f, float s) {
 }
 __device__ __forceinline__ float frag_scale(float f, float s) { return f * s; }
 
+// Per-row values of local_grad, kept at the start of its LDS so that their
+// addresses fit the LDS instructions' immediate offsets.
+struct LocSmall {
+  float gam[64];  // gamma * log2(e)
+  float eg[64];   // exp(gamma)
+  float dec[64];  // exp(gamma_L - gamma)
+  float bet[64];
+  float rowp[4][2][64];  // [de, db, rs, c][half][row]
+  float colp[4][64];     // [row tile][col]
+  float glp[kNW];
+};
+
 template <typename E, int K, int V>
 __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   using G = Geo<E, K, V>;
@@ -465,12 +484,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   constexpr int NKC = 64 / KS;
   constexpr int NKB = C::VB / KS;
   constexpr int VB = C::VB, LDB = C::LDB, NCHB = C::NCHB, NCHK = C::NCHK;
-  __shared__ __attribute__((aligned(16))) char smem_[C::bytes];
-  __shared__ __attribute__((aligned(16))) float sgam[64], seg[64], sdec[64], sbet[64];
-  __shared__ float rowp[4][2][64];  // [de, db, rs, c][half][row]
-  __shared__ float colp[4][64];     // [row tile][col]
-  __shared__ float glp[kNW];
-  E *sm = reinterpret_cast<E *>(smem_);
+  static_assert(sizeof(LocSmall) % 16 == 0, "LDS alignment");
+  __shared__ __attribute__((aligned(16))) char smem_[sizeof(LocSmall) + C::bytes];
+  LocSmall &ls = *reinterpret_cast<LocSmall *>(smem_);
+  float *sgam = ls.gam, *seg = ls.eg, *sdec = ls.dec, *sbet = ls.bet;
+  auto &rowp = ls.rowp;
+  auto &colp = ls.colp;
+  float *glp = ls.glp;
+  E *sm = reinterpret_cast<E *>(smem_ + sizeof(LocSmall));
   E *sQ = sm + C::oQ;
   E *sK = sm + C::oK;
   E *sT = sm + C::oT;
@@ -487,11 +508,20 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   E *sV = sm + C::oV;
 
   const Problem &p = a.p;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int w = wave_of(threadIdx.x);
   const int rt = w & 3, ch = w >> 2;
   const int pc0 = 2 * ch;
-  const int ra = 16 * rt + lr;  // matrix row an A-operand fragment of this lane covers
+  // Lane quantities; re-derived (opaquely) at the top of each loop iteration
+  // so that the addresses built on them are not hoisted and held across it.
+  int tid, lane, lr, lg, ra;  // ra: matrix row an A-operand fragment of this lane covers
+  auto relane = [&]() {
+    tid = opaque_tid();
+    lane = tid & 63;
+    lr = lane & 15;
+    lg = lane >> 4;
+    ra = 16 * rt + lr;
+  };
+  relane();
   const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
   const int hq = (int)(wid % p.Hq);
   const int64_t gid = wid / p.Hq;
@@ -572,6 +602,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   }
 
   for (int hl = 0; hl < Gq; ++hl) {
+    relane();
     const int h = hq * Gq + hl;
     const int64_t cg = gid * p.Hv + h;  // (chunk, v-head) slot of per-chunk buffers
     // ---- per v-head inputs: T, gates
@@ -587,11 +618,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         const int64_t gi = (tok0 + tid) * p.Hv + h;
         const float gv = tid < rows ? a.g[gi] : 0.f;
         const float bv = tid < rows ? to_f32(bp[gi]) : 0.f;
-        const float gam = wave_incl_scan(gv);
+        const float gam = wave_incl_scan(gv) * kLog2e;
         const float gL = __shfl(gam, 63, 64);
         sgam[tid] = gam;
-        seg[tid] = expf(gam);
-        sdec[tid] = expf(gL - gam);
+        seg[tid] = __builtin_amdgcn_exp2f(gam);
+        sdec[tid] = __builtin_amdgcn_exp2f(gL - gam);
         sbet[tid] = bv;
       }
     }
@@ -616,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 16 * rt + 4 * lg + i;
-        pv[i] = (t <= s) ? qk[cc][i] * expf(gam_s[i] - gt) : 0.f;
+        pv[i] = (t <= s) ? qk[cc][i] * __builtin_amdgcn_exp2f(gam_s[i] - gt) : 0.f;
       }
       st4(sPt + t * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
     }
@@ -634,6 +665,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     const E *ds = dst + cg * (int64_t)K * V;
 
     for (int vb = 0; vb < C::NVB; ++vb) {
+      relane();
       const int v0 = vb * VB;
       __syncthreads();  // previous readers of the block buffers are done
       // S, D blocks, <D, S> partial, dO block
@@ -840,7 +872,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 16 * rt + 4 * lg + i;
-        const float e = (t <= s) ? expf(gam_s[i] - gt) : 0.f;
+        const float e = (t <= s) ? __builtin_amdgcn_exp2f(gam_s[i] - gt) : 0.f;
         const float dpm = (t <= s) ? scale * dp[cc][i] : 0.f;
         const float dam = (t < s) ? -da[cc][i] : 0.f;
         pe[i] = dpm * e;

@@ -51,8 +51,9 @@ struct Mma<bf16> {
   // 16-bit elements, and output lane j receives element j & 3 of the group's
   // lanes 4e + (j >> 2), e < 4.  Source lane s of a group therefore points at
   // row (s >> 2) and columns 4*(s & 3) .. +3 of a 4 x 16 block.
-  __device__ static __forceinline__ frag ld_tr(const bf16 *tile, int ld) {
-    const int l = threadIdx.x & 63;
+  // (l: lane index; callers in long loops pass a per-iteration copy)
+  __device__ static __forceinline__ frag ld_tr(const bf16 *tile, int ld,
+                                               int l = threadIdx.x & 63) {
     const bf16 *p = tile + (8 * (l >> 4) + ((l & 15) >> 2)) * ld + 4 * (l & 3);
     typedef __attribute__((address_space(3))) bf16x4 lds4;
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4 *)p);
@@ -60,9 +61,10 @@ struct Mma<bf16> {
     return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   // ld_tr with element e scaled by w[8*(l >> 4) + e] (a factor per row k)
-  __device__ static __forceinline__ frag ld_tr_scaled(const bf16 *tile, int ld, const float *w) {
-    const frag x = ld_tr(tile, ld);
-    const float *wl = w + 8 * ((threadIdx.x & 63) >> 4);
+  __device__ static __forceinline__ frag ld_tr_scaled(const bf16 *tile, int ld, const float *w,
+                                                      int l = threadIdx.x & 63) {
+    const frag x = ld_tr(tile, ld, l);
+    const float *wl = w + 8 * (l >> 4);
     frag f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)x[e] * wl[e]);
@@ -70,8 +72,9 @@ struct Mma<bf16> {
   }
   // X[m][k] + X[k][m]: 8 contiguous elements at p (as ld) plus the k-major
   // fragment of the same tile (rounded once)
-  __device__ static __forceinline__ frag ld_sym_tr(const bf16 *p, const bf16 *tile, int pitch) {
-    const frag a = ld(p), b = ld_tr(tile, pitch);
+  __device__ static __forceinline__ frag ld_sym_tr(const bf16 *p, const bf16 *tile, int pitch,
+                                                   int l = threadIdx.x & 63) {
+    const frag a = ld(p), b = ld_tr(tile, pitch, l);
     frag f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)a[e] + (float)b[e]);
@@ -89,15 +92,17 @@ struct Mma<float> {
   }
   __device__ static __forceinline__ frag ld(const float *p) { return *p; }
   // k-major operand (see Mma<bf16>::ld_tr): lane l reads X[k0 + (l >> 4)][c0 + (l & 15)]
-  __device__ static __forceinline__ frag ld_tr(const float *tile, int ld) {
-    const int l = threadIdx.x & 63;
+  __device__ static __forceinline__ frag ld_tr(const float *tile, int ld,
+                                               int l = threadIdx.x & 63) {
     return tile[(l >> 4) * ld + (l & 15)];
   }
-  __device__ static __forceinline__ frag ld_tr_scaled(const float *tile, int ld, const float *w) {
-    return ld_tr(tile, ld) * w[(threadIdx.x & 63) >> 4];
+  __device__ static __forceinline__ frag ld_tr_scaled(const float *tile, int ld, const float *w,
+                                                      int l = threadIdx.x & 63) {
+    return ld_tr(tile, ld, l) * w[l >> 4];
   }
-  __device__ static __forceinline__ frag ld_sym_tr(const float *p, const float *tile, int ld) {
-    return p[0] + ld_tr(tile, ld);
+  __device__ static __forceinline__ frag ld_sym_tr(const float *p, const float *tile, int ld,
+                                                   int l = threadIdx.x & 63) {
+    return p[0] + ld_tr(tile, ld, l);
   }
 };
 
@@ -124,6 +129,21 @@ __device__ __forceinline__ void st4(float *p, float a, float b, float c, float d
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// The thread index as an opaque value.  Long loops take a copy at the top of
+// each iteration: address arithmetic derived from it is then recomputed inside
+// the iteration instead of being hoisted out of the loop, where the many
+// per-lane LDS addresses (regions past the 64 KB reach of the LDS immediate
+// offset each need their own register) would otherwise be spilled.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+// Wave index of a thread index, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_of(int tid) {
+  return __builtin_amdgcn_readfirstlane(tid >> 6);
+}
 
 // Inclusive prefix sum across the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_incl_scan(float x) {

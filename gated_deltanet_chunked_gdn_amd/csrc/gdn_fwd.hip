@@ -317,11 +317,11 @@ struct Smem {
 };
 
 template <typename E, int K, int V, bool WANT_V>
-__device__ __forceinline__ void fwd_commit(const Pref<E, K, V> &pf, const Smem &S) {
+__device__ __forceinline__ void fwd_commit(const Pref<E, K, V> &pf, const Smem &S,
+                                           int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
   using L = FwdLds<E, K, V>;
   E *sm = reinterpret_cast<E *>(S.base);
-  const int tid = threadIdx.x;
   constexpr int PK = K / G::VEC, PVr = V / G::VEC, PTr = 64 / G::VEC;
 #pragma unroll
   for (int m = 0; m < G::NQ; ++m) {
@@ -350,7 +350,7 @@ __device__ __forceinline__ void fwd_commit(const Pref<E, K, V> &pf, const Smem &
       *reinterpret_cast<uint4 *>(sm + L::oT + r * G::LDC + cv * G::VEC) = pf.t[m];
     }
   }
-  gate_commit(pf.g, pf.b, S.gate);
+  gate_commit(pf.g, pf.beta(), S.gate, tid);
 }
 
 // Runs chunks [c_begin, c_end) of one (sequence, v-head) starting from the
@@ -380,8 +380,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
   E *sP = sm + L::oP;
   E *sRt = sm + L::oRt;
   E *sVnt = sm + L::oVnt;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int w = wave_of(threadIdx.x);
   const int rt = w & 3;            // chunk-row tile of this wave
   const int ct0 = (w >> 2) * NCH;  // first V column tile of this wave
   const float scale = p.scale;
@@ -406,15 +405,24 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
   __syncthreads();
   bool zero_exit = false;
   for (int c = c_begin; c < c_end && !zero_exit; ++c) {
+    const int tid = opaque_tid(), lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
     const int64_t tok0 = si.tok0 + (int64_t)c * kChunk;
     const int rows = pf.rows;
     if (a.h) {
       float *hs = a.h + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
-      tiles_store<E, K, V>(st, hs, nullptr, MODE == kFix);
+      tiles_store<E, K, V>(st, hs, nullptr, MODE == kFix, tid);
     }
     if (a.h_e) {
       E *hs = reinterpret_cast<E *>(a.h_e) + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
-      tiles_store_e<E, K, V>(st, hs, MODE == kFix);
+      tiles_store_e<E, K, V>(st, hs, MODE == kFix, tid);
+    }
+    // the next chunk's inputs travel while this whole chunk is computed (this
+    // chunk's inputs were committed to LDS at the end of the previous one)
+    if (c + 1 < c_end) {
+      const int rows1 = min(kChunk, si.len - (c + 1) * kChunk);
+      pref_load<E, K, V, WANT_V>(pf, p, qp, kp, vp, tmat, a.g, bp, tok0 + kChunk, rows1, h,
+                                 chunk_gid0 + c + 1, tid);
     }
     // ---- phase A: Q S, K S (this wave's row tile, its half of V), Q K^T
     const int pc0 = 2 * (w >> 2);  // P column tiles of this wave: pc0, pc0 + 1
@@ -480,12 +488,6 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       st4(sRt + vc * G::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
     }
     __syncthreads();
-    // next chunk's inputs travel while phases B and C run
-    if (c + 1 < c_end) {
-      const int rows1 = min(kChunk, si.len - (c + 1) * kChunk);
-      pref_load<E, K, V, WANT_V>(pf, p, qp, kp, vp, tmat, a.g, bp, tok0 + kChunk, rows1, h,
-                                 chunk_gid0 + c + 1);
-    }
     // ---- phase B: Vn = T R (row tile rt, this wave's half of V)
     {
       typename M::frag ta[NKC];
@@ -525,13 +527,16 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
           qs[c2] = M::mma(
               pa[ks], M::ld(sVnt + (16 * (ct0 + c2) + lr) * G::LDC + ks * KS + EPL * lg),
               qs[c2]);
+      char *obase = reinterpret_cast<char *>(op + (tok0 * p.Hv + h) * V);
+      const uint32_t ors = (uint32_t)(p.Hv * V * sizeof(E));
 #pragma unroll
       for (int c2 = 0; c2 < NCH; ++c2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * lg + i;
           if (r < rows) {
-            E *dst = op + ((tok0 + r) * p.Hv + h) * V + 16 * (ct0 + c2) + lr;
+            E *dst = reinterpret_cast<E *>(
+                obase + (uint32_t)r * ors + (uint32_t)((16 * (ct0 + c2) + lr) * sizeof(E)));
             float val = scale * qs[c2][i];
             if (MODE == kFix) val += to_f32(*dst);
             *dst = from_f32<E>(val);
@@ -544,7 +549,8 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       typename M::frag kt[NKC];
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks) {
-        kt[ks] = M::ld_tr_scaled(sK + ks * KS * G::LDK + 16 * srt, G::LDK, S.gate.dec + ks * KS);
+        kt[ks] = M::ld_tr_scaled(sK + ks * KS * G::LDK + 16 * srt, G::LDK, S.gate.dec + ks * KS,
+                                 lane);
       }
 #pragma unroll
       for (int m = 0; m < G::NTS; ++m)
@@ -558,14 +564,14 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
                          M::ld(sVnt + (16 * (sct + m) + lr) * G::LDC + ks * KS + EPL * lg),
                          st[m]);
     }
-    tiles_to_lds_t<E, K, V>(st, sSt);
+    tiles_to_lds_t<E, K, V>(st, sSt, tid);
     if (MODE == kFix) {
       zero_exit = !block_any(tiles_nonzero<E, K, V>(st), S.flag);
     } else {
       __syncthreads();
     }
     if (c + 1 < c_end && !zero_exit) {
-      fwd_commit<E, K, V, WANT_V>(pf, S);
+      fwd_commit<E, K, V, WANT_V>(pf, S, tid);
       __syncthreads();
     }
   }

@@ -140,61 +140,71 @@ template <typename E, int K, int V>
 struct Pref {
   using G = Geo<E, K, V>;
   uint4 q[G::NQ], k[G::NQ], v[G::NV], t[G::NTM];
-  float g, b;
+  float g;
+  E b;  // raw beta: converted when committed, so its load is not waited on early
   int rows;
+  __device__ float beta() const { return to_f32(b); }
 };
 
 // Load one chunk's q, k, (v-like tile), T, g, beta into registers.
 // vsrc is v (forward) or do (backward); it is skipped when null-like (want_v).
+// Tile bases are computed once per chunk (wave-uniform, scalar registers) and
+// lanes add 32-bit byte offsets, which keeps per-lane 64-bit addresses out of
+// the registers that stay live while the loads are in flight.
 template <typename E, int K, int V, bool WANT_V>
 __device__ __forceinline__ void pref_load(Pref<E, K, V> &pf, const Problem &p, const E *qp,
                                           const E *kp, const E *vsrc, const E *tmat,
                                           const float *g, const E *beta, int64_t tok0,
-                                          int rows, int h, int64_t cgid) {
+                                          int rows, int h, int64_t cgid,
+                                          int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
-  const int tid = threadIdx.x;
   const int hq = h / (p.Hv / p.Hq);
   constexpr int PK = K / G::VEC, PVr = V / G::VEC;
   pf.rows = rows;
+  const char *qb = reinterpret_cast<const char *>(qp + (tok0 * p.Hq + hq) * K);
+  const char *kb = reinterpret_cast<const char *>(kp + (tok0 * p.Hq + hq) * K);
+  const uint32_t qrs = (uint32_t)(p.Hq * K * sizeof(E));  // bytes between token rows
 #pragma unroll
   for (int m = 0; m < G::NQ; ++m) {
     const int idx = tid + kThreads * m;
     const int r = idx / PK, cv = idx % PK;
     uint4 zq = make_uint4(0u, 0u, 0u, 0u), zk = zq;
     if (idx < G::PQ && r < rows) {
-      const int64_t off = ((tok0 + r) * p.Hq + hq) * K + cv * G::VEC;
-      zq = *reinterpret_cast<const uint4 *>(qp + off);
-      zk = *reinterpret_cast<const uint4 *>(kp + off);
+      const uint32_t off = (uint32_t)r * qrs + (uint32_t)cv * 16u;
+      zq = *reinterpret_cast<const uint4 *>(qb + off);
+      zk = *reinterpret_cast<const uint4 *>(kb + off);
     }
     pf.q[m] = zq;
     pf.k[m] = zk;
   }
   if (WANT_V) {
+    const char *vb = reinterpret_cast<const char *>(vsrc + (tok0 * p.Hv + h) * V);
+    const uint32_t vrs = (uint32_t)(p.Hv * V * sizeof(E));
 #pragma unroll
     for (int m = 0; m < G::NV; ++m) {
       const int idx = tid + kThreads * m;
       const int r = idx / PVr, cv = idx % PVr;
       uint4 z = make_uint4(0u, 0u, 0u, 0u);
       if (idx < G::PV && r < rows)
-        z = *reinterpret_cast<const uint4 *>(vsrc + ((tok0 + r) * p.Hv + h) * V +
-                                             cv * G::VEC);
+        z = *reinterpret_cast<const uint4 *>(vb + (uint32_t)r * vrs + (uint32_t)cv * 16u);
       pf.v[m] = z;
     }
   }
-  const E *tm = tmat + (cgid * p.Hv + h) * 64 * 64;
+  const char *tm = reinterpret_cast<const char *>(tmat + (cgid * p.Hv + h) * 64 * 64);
 #pragma unroll
   for (int m = 0; m < G::NTM; ++m) {
     const int idx = tid + kThreads * m;
     uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    if (idx < G::PT) z = *reinterpret_cast<const uint4 *>(tm + idx * G::VEC);
+    if (idx < G::PT) z = *reinterpret_cast<const uint4 *>(tm + (uint32_t)idx * 16u);
     pf.t[m] = z;
   }
   pf.g = 0.f;
-  pf.b = 0.f;
+  pf.b = from_f32<E>(0.f);
   if (tid < 64 && tid < rows) {
-    const int64_t gi = (tok0 + tid) * p.Hv + h;
-    pf.g = g[gi];
-    pf.b = to_f32(beta[gi]);
+    const int64_t gi0 = tok0 * p.Hv + h;
+    const uint32_t gi = (uint32_t)tid * (uint32_t)p.Hv;
+    pf.g = g[gi0 + gi];
+    pf.b = beta[gi0 + gi];
   }
 }
 
@@ -207,8 +217,8 @@ struct GateLds {
 };
 
 // Wave 0 turns the prefetched g, beta into the gate quantities.
-__device__ __forceinline__ void gate_commit(float g, float b, const GateLds &G) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void gate_commit(float g, float b, const GateLds &G,
+                                            int tid = threadIdx.x) {
   if (tid < 64) {
     const float gam = wave_incl_scan(g) * kLog2e;
     const float gL = __shfl(gam, 63, 64);
@@ -231,9 +241,10 @@ __device__ __forceinline__ void tiles_zero(Tiles<Geo<E, K, V>::NTS> &s) {
 
 // Read a global fp32 [K][V] matrix (or zeros if src is null) into the tiles.
 template <typename E, int K, int V>
-__device__ __forceinline__ void tiles_load(Tiles<Geo<E, K, V>::NTS> &s, const float *src) {
+__device__ __forceinline__ void tiles_load(Tiles<Geo<E, K, V>::NTS> &s, const float *src,
+    int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_of(tid), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int m = 0; m < G::NTS; ++m) {
@@ -250,9 +261,10 @@ __device__ __forceinline__ void tiles_load(Tiles<Geo<E, K, V>::NTS> &s, const fl
 // dst = tiles (+ add[] if given) (+ dst if accumulate).
 template <typename E, int K, int V>
 __device__ __forceinline__ void tiles_store(const Tiles<Geo<E, K, V>::NTS> &s, float *dst,
-                                            const float *add, bool accumulate) {
+                                            const float *add, bool accumulate,
+    int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_of(tid), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   if (!G::owns(w)) return;
   const int rt = G::srt(w);
@@ -261,7 +273,8 @@ __device__ __forceinline__ void tiles_store(const Tiles<Geo<E, K, V>::NTS> &s, f
     const int ct = G::sct(w) + m;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t off = (16 * rt + 4 * lg + i) * V + 16 * ct + lr;
+      // 32-bit element offset from the (wave-uniform) matrix base
+      const uint32_t off = (uint32_t)((16 * rt + 4 * lg + i) * V + 16 * ct + lr);
       float x = s[m][i];
       if (add) x += add[off];
       if (accumulate) x += dst[off];
@@ -274,9 +287,10 @@ __device__ __forceinline__ void tiles_store(const Tiles<Geo<E, K, V>::NTS> &s, f
 // dst = tiles (+ dst if accumulate), rounded once to E.
 template <typename E, int K, int V>
 __device__ __forceinline__ void tiles_store_e(const Tiles<Geo<E, K, V>::NTS> &s, E *dst,
-                                              bool accumulate) {
+                                              bool accumulate,
+    int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_of(tid), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   if (!G::owns(w)) return;
   const int rt = G::srt(w);
@@ -285,7 +299,7 @@ __device__ __forceinline__ void tiles_store_e(const Tiles<Geo<E, K, V>::NTS> &s,
     const int ct = G::sct(w) + m;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t off = (16 * rt + 4 * lg + i) * V + 16 * ct + lr;
+      const uint32_t off = (uint32_t)((16 * rt + 4 * lg + i) * V + 16 * ct + lr);
       float x = s[m][i];
       if (accumulate) x += to_f32(dst[off]);
       dst[off] = from_f32<E>(x);
@@ -295,9 +309,10 @@ __device__ __forceinline__ void tiles_store_e(const Tiles<Geo<E, K, V>::NTS> &s,
 
 // Transposed working copy (element type) in LDS: dstT[v][i] = S[i][v].
 template <typename E, int K, int V>
-__device__ __forceinline__ void tiles_to_lds_t(const Tiles<Geo<E, K, V>::NTS> &s, E *dstT) {
+__device__ __forceinline__ void tiles_to_lds_t(const Tiles<Geo<E, K, V>::NTS> &s, E *dstT,
+    int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_of(tid), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   if (!G::owns(w)) return;
   const int rt = G::srt(w);
