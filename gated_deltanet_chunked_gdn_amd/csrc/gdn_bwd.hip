@@ -424,15 +424,21 @@ struct LocCfg {
   static constexpr int oK = oQ + 64 * G::LDK;
   static constexpr int oT = oK + 64 * G::LDK;
   static constexpr int oPt = oT + 64 * G::LDC;
+  // V-block buffers (dead after the V-block loop)
   static constexpr int oS = oPt + 64 * G::LDC;     // S block [K][LDB]
   static constexpr int oD = oS + K * LDB;          // D block [K][LDB]; later dR [64][LDB]
   static constexpr int oDO = oD + (K > 64 ? K : 64) * LDB;  // dO block [64][LDB]
-  static constexpr int oRt = oDO + 64 * LDB;       // R^T [VB][LDC]; later dVn^T
+  static constexpr int oDOq = oDO + 64 * LDB;      // dO rows * scale e^gamma
+  static constexpr int oRt = oDOq + 64 * LDB;      // R^T [VB][LDC]; later dVn^T
   static constexpr int oVn = oRt + VB * G::LDC;    // Vn [64][LDB]
-  static constexpr int oPE = oVn + 64 * LDB;       // dP * E [64][LDC]
-  static constexpr int oKK = oPE + 64 * G::LDC;    // dKK [64][LDC]
-  static constexpr int oV = oKK + 64 * G::LDC;     // V block [64][LDB]
+  static constexpr int oVnd = oVn + 64 * LDB;      // Vn rows * e^{gamma_L - gamma}
+  static constexpr int oDRs = oVnd + 64 * LDB;     // dR rows * (-beta e^gamma)
+  static constexpr int oV = oDRs + 64 * LDB;       // V block [64][LDB]
   static constexpr int nE = oV + 64 * LDB;
+  // after the V-block loop: dP * E and dKK [64][LDC] reuse the block buffers
+  static constexpr int oPE = oS;
+  static constexpr int oKK = oPE + 64 * G::LDC;
+  static_assert(oKK + 64 * G::LDC <= nE, "LDS reuse");
   static constexpr int bytes = nE * (int)sizeof(E);
 };
 
@@ -452,15 +458,16 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// An MFMA A-operand fragment belongs to one matrix row per lane: scaling the
-// fragment by that row's factor scales the product's row.
-__device__ __forceinline__ bf16x8 frag_scale(bf16x8 f, float s) {
-  bf16x8 r;
+// A 16-byte piece of element type E with every element times s (rounded once).
+template <typename E>
+__device__ __forceinline__ uint4 scale_piece(const uint4 &x, float s) {
+  uint4 r;
+  const E *a = reinterpret_cast<const E *>(&x);
+  E *b = reinterpret_cast<E *>(&r);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)((float)f[e] * s);
+  for (int e = 0; e < 16 / (int)sizeof(E); ++e) b[e] = from_f32<E>(to_f32(a[e]) * s);
   return r;
 }
-__device__ __forceinline__ float frag_scale(float f, float s) { return f * s; }
 
 // Per-row values of local_grad, kept at the start of its LDS so that their
 // addresses fit the LDS instructions' immediate offsets.
@@ -472,6 +479,21 @@ struct LocSmall {
   float rowp[4][2][64];  // [de, db, rs, c][half][row]
   float colp[4][64];     // [row tile][col]
   float glp[kNW];
+};
+
+// Registers that carry the next V block (S, D, dO, V pieces) and, at a v-head
+// boundary, the next v-head's T piece and raw g, beta while the current block
+// is computed.
+template <typename E, int K, int V>
+struct LocPref {
+  using C = LocCfg<E, K, V>;
+  static constexpr int PB = C::VB * (int)sizeof(E) / 16;  // 16-byte pieces per block row
+  static constexpr int NSP = (K * PB + kThreads - 1) / kThreads;
+  static constexpr int NOP = (64 * PB + kThreads - 1) / kThreads;
+  static constexpr int NTP = (64 * 64 * (int)sizeof(E) / 16 + kThreads - 1) / kThreads;
+  uint4 s[NSP], d[NSP], o[NOP], v[NOP], t[NTP];
+  float g;
+  E b;
 };
 
 template <typename E, int K, int V>
@@ -503,6 +525,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   E *sRt = sm + C::oRt;
   E *sDVnt = sm + C::oRt;
   E *sVn = sm + C::oVn;
+  E *sDOq = sm + C::oDOq;
+  E *sVnd = sm + C::oVnd;
+  E *sDRs = sm + C::oDRs;
   E *sPE = sm + C::oPE;
   E *sKK = sm + C::oKK;
   E *sV = sm + C::oV;
@@ -601,39 +626,92 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     dk[m] = zero4();
   }
 
+  using LP = LocPref<E, K, V>;
+  constexpr int PB = LP::PB;
+  LP pf;
+  // global loads of V block vb of v-head hl (rows past the chunk end read 0)
+  auto load_block = [&](int hl, int vb) {
+    const int h = hq * Gq + hl;
+    const int64_t cg = gid * p.Hv + h;
+    const int v0 = vb * VB;
+    const char *hsb = reinterpret_cast<const char *>(hst + cg * (int64_t)K * V + v0);
+    const char *dsb = reinterpret_cast<const char *>(dst + cg * (int64_t)K * V + v0);
+#pragma unroll
+    for (int m = 0; m < LP::NSP; ++m) {
+      const int idx = tid + kThreads * m;
+      const int i = idx / PB, cv = idx % PB;
+      uint4 zs = make_uint4(0u, 0u, 0u, 0u), zd = zs;
+      if (idx < K * PB) {
+        const uint32_t off = (uint32_t)((i * V + cv * VEC) * sizeof(E));
+        zs = *reinterpret_cast<const uint4 *>(hsb + off);
+        zd = *reinterpret_cast<const uint4 *>(dsb + off);
+      }
+      pf.s[m] = zs;
+      pf.d[m] = zd;
+    }
+    const char *vb_ = reinterpret_cast<const char *>(vp + (tok0 * p.Hv + h) * V + v0);
+    const char *ob_ = reinterpret_cast<const char *>(dop + (tok0 * p.Hv + h) * V + v0);
+#pragma unroll
+    for (int m = 0; m < LP::NOP; ++m) {
+      const int idx = tid + kThreads * m;
+      const int r = idx / PB, cv = idx % PB;
+      uint4 zo = make_uint4(0u, 0u, 0u, 0u), zv = zo;
+      if (idx < 64 * PB && r < rows) {
+        const uint32_t off = r * v_rs + (uint32_t)(cv * 16);
+        zo = *reinterpret_cast<const uint4 *>(ob_ + off);
+        zv = *reinterpret_cast<const uint4 *>(vb_ + off);
+      }
+      pf.o[m] = zo;
+      pf.v[m] = zv;
+    }
+  };
+  // global loads of v-head hl's T and raw gates
+  auto load_head = [&](int hl) {
+    const int h = hq * Gq + hl;
+    const int64_t cg = gid * p.Hv + h;
+    const char *tm = reinterpret_cast<const char *>(tmat + cg * 64 * 64);
+#pragma unroll
+    for (int m = 0; m < LP::NTP; ++m) {
+      const int idx = tid + kThreads * m;
+      pf.t[m] = idx < 64 * 64 / VEC ? *reinterpret_cast<const uint4 *>(tm + idx * 16)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+    pf.g = 0.f;
+    pf.b = from_f32<E>(0.f);
+    if (tid < rows) {
+      const int64_t gi = (tok0 + tid) * p.Hv + h;
+      pf.g = a.g[gi];
+      pf.b = bp[gi];
+    }
+  };
+  load_head(0);
+  load_block(0, 0);
+
   for (int hl = 0; hl < Gq; ++hl) {
     relane();
     const int h = hq * Gq + hl;
-    const int64_t cg = gid * p.Hv + h;  // (chunk, v-head) slot of per-chunk buffers
-    // ---- per v-head inputs: T, gates
+    // ---- per v-head inputs: T, gates (from the prefetch registers)
     {
-      const E *tm = tmat + cg * 64 * 64;
       constexpr int PT = 64 / VEC;
-      for (int idx = tid; idx < 64 * PT; idx += kThreads) {
-        const int r = idx / PT, cv = idx % PT;
-        *reinterpret_cast<uint4 *>(sT + r * G::LDC + cv * VEC) =
-            *reinterpret_cast<const uint4 *>(tm + r * 64 + cv * VEC);
+#pragma unroll
+      for (int m = 0; m < LP::NTP; ++m) {
+        const int idx = tid + kThreads * m;
+        if (idx < 64 * PT) {
+          const int r = idx / PT, cv = idx % PT;
+          *reinterpret_cast<uint4 *>(sT + r * G::LDC + cv * VEC) = pf.t[m];
+        }
       }
       if (tid < 64) {
-        const int64_t gi = (tok0 + tid) * p.Hv + h;
-        const float gv = tid < rows ? a.g[gi] : 0.f;
-        const float bv = tid < rows ? to_f32(bp[gi]) : 0.f;
-        const float gam = wave_incl_scan(gv) * kLog2e;
+        const float gam = wave_incl_scan(pf.g) * kLog2e;
         const float gL = __shfl(gam, 63, 64);
         sgam[tid] = gam;
         seg[tid] = __builtin_amdgcn_exp2f(gam);
         sdec[tid] = __builtin_amdgcn_exp2f(gL - gam);
-        sbet[tid] = bv;
+        sbet[tid] = to_f32(pf.b);
       }
     }
     __syncthreads();
-    const char *vtile = reinterpret_cast<const char *>(vp + (tok0 * p.Hv + h) * V);
-    const char *dotile = reinterpret_cast<const char *>(dop + (tok0 * p.Hv + h) * V);
     char *dvtile = reinterpret_cast<char *>(dvp + (tok0 * p.Hv + h) * V);
-    // row factors of this lane's A-operand row
-    const float f_q = scale * seg[ra];            // dq  += (scale e^g dO) S^T
-    const float f_r = -sbet[ra] * seg[ra];        // dk  += (-beta e^g dR) S^T
-    const float f_v = sdec[ra];                   // dk  += (e^{gL-g} Vn) D^T
     // P^T (P = lower_incl(Q K^T * E)) of this v-head into LDS
     {
     f32x4 qk[2];
@@ -661,38 +739,43 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     float de_p[4] = {0.f, 0.f, 0.f, 0.f}, db_p[4] = {0.f, 0.f, 0.f, 0.f};
     float c_p[4] = {0.f, 0.f, 0.f, 0.f};
     float gl_p = 0.f;
-    const E *hs = hst + cg * (int64_t)K * V;
-    const E *ds = dst + cg * (int64_t)K * V;
 
     for (int vb = 0; vb < C::NVB; ++vb) {
       relane();
       const int v0 = vb * VB;
       __syncthreads();  // previous readers of the block buffers are done
-      // S, D blocks, <D, S> partial, dO block
+      // commit the prefetched S, D, dO, V block; <D, S> partial; scaled dO
       {
-        constexpr int PB = VB / VEC;
-        for (int idx = tid; idx < K * PB; idx += kThreads) {
-          const int i = idx / PB, cv = idx % PB;
-          const uint4 s4 = *reinterpret_cast<const uint4 *>(hs + (int64_t)i * V + v0 + cv * VEC);
-          const uint4 d4 = *reinterpret_cast<const uint4 *>(ds + (int64_t)i * V + v0 + cv * VEC);
-          const E *se = reinterpret_cast<const E *>(&s4);
-          const E *de = reinterpret_cast<const E *>(&d4);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) gl_p += to_f32(se[e]) * to_f32(de[e]);
-          *reinterpret_cast<uint4 *>(sS + i * LDB + cv * VEC) = s4;
-          *reinterpret_cast<uint4 *>(sD + i * LDB + cv * VEC) = d4;
-        }
-        for (int idx = tid; idx < 64 * PB; idx += kThreads) {
-          const int r = idx / PB, cv = idx % PB;
-          uint4 z = make_uint4(0u, 0u, 0u, 0u), zv = z;
-          if (r < rows) {
-            const uint32_t off = r * v_rs + (uint32_t)((v0 + cv * VEC) * sizeof(E));
-            z = *reinterpret_cast<const uint4 *>(dotile + off);
-            zv = *reinterpret_cast<const uint4 *>(vtile + off);
+        for (int m = 0; m < LP::NSP; ++m) {
+          const int idx = tid + kThreads * m;
+          if (idx < K * PB) {
+            const int i = idx / PB, cv = idx % PB;
+            gl_p = dot_piece<E>(pf.s[m], pf.d[m], gl_p);
+            *reinterpret_cast<uint4 *>(sS + i * LDB + cv * VEC) = pf.s[m];
+            *reinterpret_cast<uint4 *>(sD + i * LDB + cv * VEC) = pf.d[m];
           }
-          *reinterpret_cast<uint4 *>(sDO + r * LDB + cv * VEC) = z;
-          *reinterpret_cast<uint4 *>(sV + r * LDB + cv * VEC) = zv;
         }
+#pragma unroll
+        for (int m = 0; m < LP::NOP; ++m) {
+          const int idx = tid + kThreads * m;
+          if (idx < 64 * PB) {
+            const int r = idx / PB, cv = idx % PB;
+            *reinterpret_cast<uint4 *>(sDO + r * LDB + cv * VEC) = pf.o[m];
+            // dq += (scale e^g dO) S^T takes dO with its rows scaled
+            *reinterpret_cast<uint4 *>(sDOq + r * LDB + cv * VEC) =
+                scale_piece<E>(pf.o[m], scale * seg[r]);
+            *reinterpret_cast<uint4 *>(sV + r * LDB + cv * VEC) = pf.v[m];
+          }
+        }
+      }
+      // the next block (and at a v-head boundary the next T and gates) is
+      // loaded while this one is computed
+      if (vb + 1 < C::NVB) {
+        load_block(hl, vb + 1);
+      } else if (hl + 1 < Gq) {
+        load_head(hl + 1);
+        load_block(hl + 1, 0);
       }
       __syncthreads();
       // ---- phase 2: K S, Q S; R; dq += (scale e^g dO) S^T
@@ -731,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
-        const auto da_ = frag_scale(M::ld(sDO + ra * LDB + ks * KS + EPL * lg), f_q);
+        const auto da_ = M::ld(sDOq + ra * LDB + ks * KS + EPL * lg);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
           dq[m] = M::mma(da_, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
@@ -773,6 +856,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             sVn[(16 * rt + 4 * lg + i) * LDB + vc] = from_f32<E>(vn[m][i]);
+            // dk += (e^{gL-g} Vn) D^T takes Vn with its rows scaled
+            sVnd[(16 * rt + 4 * lg + i) * LDB + vc] = from_f32<E>(dec_s[i] * vn[m][i]);
             c_p[i] += dec_s[i] * vn[m][i] * kd[m][i];
           }
         }
@@ -802,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       // ---- phase 4b: dk += (dec Vn) D^T;  phase 5: dR = T^T dVn, dv, dbeta/de rows
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
-        const auto vna = frag_scale(M::ld(sVn + ra * LDB + ks * KS + EPL * lg), f_v);
+        const auto vna = M::ld(sVnd + ra * LDB + ks * KS + EPL * lg);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
           dk[m] = M::mma(vna, M::ld(sD + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
@@ -831,6 +916,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           const int s = 16 * rt + 4 * lg + i;
           const float x = dr[m][i];
           sDR[s * LDB + vc] = from_f32<E>(x);
+          // dk += (-beta e^g dR) S^T takes dR with its rows scaled
+          sDRs[s * LDB + vc] = from_f32<E>(-bet_s[i] * eg_s[i] * x);
           if (s < rows)
             *reinterpret_cast<E *>(dvtile + s * v_rs + (uint32_t)((v0 + vc) * sizeof(E))) =
                 from_f32<E>(bet_s[i] * x);
@@ -852,13 +939,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
             dp[cc] = M::mma(doa, vnb, dp[cc]);
             da[cc] = M::mma(dra, vnb, da[cc]);
           }
-        const auto drs = frag_scale(dra, f_r);
+        const auto drs = M::ld(sDRs + ra * LDB + ks * KS + EPL * lg);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
           dk[m] = M::mma(drs, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
                          dk[m]);
       }
     }
+    __syncthreads();  // the block buffers are free: dP*E and dKK reuse them
     // ---- phase 7: masks, dP*E, dKK, dgamma row/column terms
     float rs_p[4] = {0.f, 0.f, 0.f, 0.f};
     f32x4 qk[2], kk[2];

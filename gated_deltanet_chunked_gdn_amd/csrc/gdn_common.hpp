@@ -115,6 +115,28 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// c + the dot product of two 16-byte pieces of element type E (8 bf16 pairs
+// through v_dot2 with fp32 accumulation, or 4 fp32 pairs).
+template <typename E>
+__device__ __forceinline__ float dot_piece(const uint4 &a, const uint4 &b, float c);
+template <>
+__device__ __forceinline__ float dot_piece<bf16>(const uint4 &a, const uint4 &b, float c) {
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 *x = reinterpret_cast<const bf16x2 *>(&a);
+  const bf16x2 *y = reinterpret_cast<const bf16x2 *>(&b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_fdot2_f32_bf16(x[e], y[e], c, false);
+  return c;
+}
+template <>
+__device__ __forceinline__ float dot_piece<float>(const uint4 &a, const uint4 &b, float c) {
+  const float *x = reinterpret_cast<const float *>(&a);
+  const float *y = reinterpret_cast<const float *>(&b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c += x[e] * y[e];
+  return c;
+}
+
 // Store 4 consecutive elements (8 bytes for bf16, 16 for fp32).
 __device__ __forceinline__ void st4(bf16 *p, float a, float b, float c, float d) {
   bf16x4 v;
