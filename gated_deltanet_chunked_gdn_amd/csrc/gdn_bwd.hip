@@ -802,12 +802,13 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < NCHB; ++m) {
         const int vc = 16 * (ch * NCHB + m) + lr;
+        const f32x4 v4 = M::ld_acc(sV + 16 * rt * LDB + 16 * (ch * NCHB + m), LDB, lane);
+        const f32x4 o4 = M::ld_acc(sDO + 16 * rt * LDB + 16 * (ch * NCHB + m), LDB, lane);
         float rr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int s = 16 * rt + 4 * lg + i;
-          rr[i] = bet_s[i] * (to_f32(sV[s * LDB + vc]) - eg_s[i] * ks_[m][i]);
-          de_p[i] += scale * to_f32(sDO[s * LDB + vc]) * qs_[m][i];
+          rr[i] = bet_s[i] * (v4[i] - eg_s[i] * ks_[m][i]);
+          de_p[i] += scale * o4[i] * qs_[m][i];
         }
         st4(sRt + vc * G::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
       }
@@ -911,6 +912,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < NCHB; ++m) {
         const int vc = 16 * (ch * NCHB + m) + lr;
+        const f32x4 v4 = M::ld_acc(sV + 16 * rt * LDB + 16 * (ch * NCHB + m), LDB, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * rt + 4 * lg + i;
@@ -921,7 +923,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           if (s < rows)
             *reinterpret_cast<E *>(dvtile + s * v_rs + (uint32_t)((v0 + vc) * sizeof(E))) =
                 from_f32<E>(bet_s[i] * x);
-          db_p[i] += x * (to_f32(sV[s * LDB + vc]) - eg_s[i] * ks_[m][i]);
+          db_p[i] += x * (v4[i] - eg_s[i] * ks_[m][i]);
           de_p[i] -= bet_s[i] * x * ks_[m][i];
         }
       }

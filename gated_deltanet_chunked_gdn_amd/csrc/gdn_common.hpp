@@ -60,6 +60,18 @@ struct Mma<bf16> {
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4 *)(p + 4 * ld));
     return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
+  // The 4 values at this lane's accumulator positions, X[r0 + 4*(l >> 4) + e]
+  // [c0 + (l & 15)] for e < 4, of a row-major tile (`tile` = &X[r0][c0],
+  // c0 % 4 == 0, ld % 4 == 0), from one transpose read: source lane s of
+  // each 16-lane group points at row 4*(l >> 4) + (s >> 2), columns
+  // 4*(s & 3) .. +3.
+  __device__ static __forceinline__ f32x4 ld_acc(const bf16 *tile, int ld,
+                                                 int l = threadIdx.x & 63) {
+    const bf16 *p = tile + (4 * (l >> 4) + ((l & 15) >> 2)) * ld + 4 * (l & 3);
+    typedef __attribute__((address_space(3))) bf16x4 lds4;
+    const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4 *)p);
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+  }
   // ld_tr with element e scaled by w[8*(l >> 4) + e] (a factor per row k)
   __device__ static __forceinline__ frag ld_tr_scaled(const bf16 *tile, int ld, const float *w,
                                                       int l = threadIdx.x & 63) {
@@ -91,6 +103,11 @@ struct Mma<float> {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ frag ld(const float *p) { return *p; }
+  __device__ static __forceinline__ f32x4 ld_acc(const float *tile, int ld,
+                                                 int l = threadIdx.x & 63) {
+    const float *p = tile + 4 * (l >> 4) * ld + (l & 15);
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+  }
   // k-major operand (see Mma<bf16>::ld_tr): lane l reads X[k0 + (l >> 4)][c0 + (l & 15)]
   __device__ static __forceinline__ frag ld_tr(const float *tile, int ld,
                                                int l = threadIdx.x & 63) {

@@ -303,8 +303,8 @@ struct FwdLds {
   static constexpr int oV = oK + 64 * G::LDK;
   static constexpr int oSt = oV + 64 * G::LDV;
   static constexpr int oT = oSt + V * G::LDK;
-  static constexpr int oP = oT + 64 * G::LDC;
-  static constexpr int oRt = oP + 64 * G::LDC;
+  static constexpr int oPt = oT + 64 * G::LDC;  // P^T [64][64]
+  static constexpr int oRt = oPt + 64 * G::LDC;
   static constexpr int oVnt = oRt + V * G::LDC;
   static constexpr int nE = oVnt + V * G::LDC;
   static constexpr int bytes = nE * (int)sizeof(E);
@@ -377,7 +377,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
   const E *sV = sm + L::oV;
   E *sSt = sm + L::oSt;
   const E *sT = sm + L::oT;
-  E *sP = sm + L::oP;
+  E *sPt = sm + L::oPt;
   E *sRt = sm + L::oRt;
   E *sVnt = sm + L::oVnt;
   const int w = wave_of(threadIdx.x);
@@ -424,7 +424,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       pref_load<E, K, V, WANT_V>(pf, p, qp, kp, vp, tmat, a.g, bp, tok0 + kChunk, rows1, h,
                                  chunk_gid0 + c + 1, tid);
     }
-    // ---- phase A: Q S, K S (this wave's row tile, its half of V), Q K^T
+    // ---- phase A: (Q S)^T, K S (this wave's row tile, its half of V), Q K^T
     const int pc0 = 2 * (w >> 2);  // P column tiles of this wave: pc0, pc0 + 1
     f32x4 qs[NCH], kss[NCH];
     f32x4 qk[2] = {zero4(), zero4()};
@@ -440,7 +440,9 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
 #pragma unroll
       for (int c2 = 0; c2 < NCH; ++c2) {
         const auto b = M::ld(sSt + (16 * (ct0 + c2) + lr) * G::LDK + ks * KS + EPL * lg);
-        if (WRITE_O) qs[c2] = M::mma(qa, b, qs[c2]);
+        // the output is built transposed (rows v, columns r): each lane then
+        // holds 4 consecutive values of one output row
+        if (WRITE_O) qs[c2] = M::mma(b, qa, qs[c2]);
         kss[c2] = M::mma(ka, b, kss[c2]);
       }
       if (WRITE_O) {
@@ -459,7 +461,8 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       b_r[i] = S.gate.bet[r];
     }
     if (WRITE_O) {
-      // P = lower_incl(Q K^T * E): this wave does column tiles pc0, pc0 + 1
+      // P = lower_incl(Q K^T * E), stored transposed: this wave does column
+      // tiles pc0, pc0 + 1 of its row tile
       float gam_r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) gam_r[i] = S.gate.gam[16 * rt + 4 * lg + i];
@@ -467,24 +470,23 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       for (int cc = 0; cc < 2; ++cc) {
         const int j = 16 * (pc0 + cc) + lr;
         const float gj = S.gate.gam[j];
+        float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * lg + i;
-          const float val = (j <= r) ? qk[cc][i] * __builtin_amdgcn_exp2f(gam_r[i] - gj) : 0.f;
-          sP[r * G::LDC + j] = from_f32<E>(val);
+          pv[i] = (j <= r) ? qk[cc][i] * __builtin_amdgcn_exp2f(gam_r[i] - gj) : 0.f;
         }
+        st4(sPt + j * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
       }
     }
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) {
       const int vc = 16 * (ct0 + c2) + lr;
+      const f32x4 vv =
+          WANT_V ? M::ld_acc(sV + 16 * rt * G::LDV + 16 * (ct0 + c2), G::LDV, lane) : zero4();
       float rr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        const float vv = WANT_V ? to_f32(sV[r * G::LDV + vc]) : 0.f;
-        rr[i] = b_r[i] * (vv - eg_r[i] * kss[c2][i]);
-      }
+      for (int i = 0; i < 4; ++i) rr[i] = b_r[i] * (vv[i] - eg_r[i] * kss[c2][i]);
       st4(sRt + vc * G::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
     }
     __syncthreads();
@@ -512,36 +514,37 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
     __syncthreads();
     // ---- phase C: output rows of this wave, state update of its tiles
     if (WRITE_O) {
-      typename M::frag pa[NKC];
+      // O^T = diag-scaled (Q S)^T + Vn^T P^T: P as the B operand (column r,
+      // contraction over j) comes from P^T by transpose reads
+      typename M::frag pb[NKC];
 #pragma unroll
-      for (int ks = 0; ks < NKC; ++ks)
-        pa[ks] = M::ld(sP + (16 * rt + lr) * G::LDC + ks * KS + EPL * lg);
+      for (int ks = 0; ks < NKC; ++ks) pb[ks] = M::ld_tr(sPt + ks * KS * G::LDC + 16 * rt, G::LDC, lane);
+      const int r = 16 * rt + lr;  // the output row this lane holds
+      const float eg_c = S.gate.eg[r];
 #pragma unroll
       for (int c2 = 0; c2 < NCH; ++c2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qs[c2][i] *= eg_r[i];
+        for (int i = 0; i < 4; ++i) qs[c2][i] *= eg_c;
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks)
 #pragma unroll
         for (int c2 = 0; c2 < NCH; ++c2)
-          qs[c2] = M::mma(
-              pa[ks], M::ld(sVnt + (16 * (ct0 + c2) + lr) * G::LDC + ks * KS + EPL * lg),
-              qs[c2]);
-      char *obase = reinterpret_cast<char *>(op + (tok0 * p.Hv + h) * V);
-      const uint32_t ors = (uint32_t)(p.Hv * V * sizeof(E));
+          qs[c2] = M::mma(M::ld(sVnt + (16 * (ct0 + c2) + lr) * G::LDC + ks * KS + EPL * lg),
+                          pb[ks], qs[c2]);
+      if (r < rows) {
+        char *orow = reinterpret_cast<char *>(op + (tok0 * p.Hv + h) * V) +
+                     (uint32_t)r * (uint32_t)(p.Hv * V * sizeof(E));
 #pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2)
+        for (int c2 = 0; c2 < NCH; ++c2) {
+          E *dst = reinterpret_cast<E *>(orow + (uint32_t)((16 * (ct0 + c2) + 4 * lg) * sizeof(E)));
+          f32x4 val = qs[c2] * scale;
+          if (MODE == kFix) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * lg + i;
-          if (r < rows) {
-            E *dst = reinterpret_cast<E *>(
-                obase + (uint32_t)r * ors + (uint32_t)((16 * (ct0 + c2) + lr) * sizeof(E)));
-            float val = scale * qs[c2][i];
-            if (MODE == kFix) val += to_f32(*dst);
-            *dst = from_f32<E>(val);
+            for (int i = 0; i < 4; ++i) val[i] += to_f32(dst[i]);
           }
+          st4(dst, val[0], val[1], val[2], val[3]);
         }
+      }
     }
     if (G::owns(w)) {
       const float egL = S.gate.eg[63];

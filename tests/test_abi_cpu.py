@@ -37,11 +37,12 @@ def ws(p):
     return gdn.lib().gdn_chunk_fwd_workspace_size(ctypes.byref(p))
 
 
-def fwd_rc(p, ptr=16, wsb=1 << 30, workspace=1 << 20):
+def fwd_rc(p, ptr=16, wsb=1 << 30, workspace=1 << 20, o=None):
     L = gdn.lib()
     P = ctypes.c_void_p
     return L.gdn_chunk_fwd(ctypes.byref(p), P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), None,
-                           P(ptr), None, None, None, None, P(workspace), wsb, None)
+                           P(ptr if o is None else o), None, None, None, None, P(workspace),
+                           wsb, None)
 
 
 def test_valid_problem_sizes():
@@ -90,6 +91,7 @@ def test_null_and_misaligned_pointers_and_workspace():
                          None, None, None, None, P(1 << 20), 1 << 30, None)
     assert rc == 1
     assert fwd_rc(p, ptr=18) == 3                 # q not 16-byte aligned
+    assert fwd_rc(p, o=20) == 3                   # o written with 8/16-byte stores
     assert fwd_rc(p, wsb=16) == 4                  # workspace too small
     assert fwd_rc(p, workspace=0) == 4             # no workspace
     assert fwd_rc(p, workspace=(1 << 20) + 64) == 4  # workspace misaligned
