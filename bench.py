@@ -130,6 +130,64 @@ def cpu_baseline(w, p, threads_hint=0):
                       f"groups), T={w.T}, fp64 token recurrence; {dt:.1f} s wall"}
 
 
+def _timer(torch):
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n
+    return timed
+
+
+def sweep(gdn, synth, torch, dev, args):
+    """Head-count sweep (the pages' TP1..TP8 axis): per H_v, the fwd+bwd step
+    with the automatic segment length, and fwd / bwd alone for a range of
+    forced segment lengths (cp_mode n = n chunks per segment, 0 = no split),
+    which is what the automatic choice is checked against."""
+    timed = _timer(torch)
+    out = []
+    for hv in synth.SWEEP_HV:
+        w = synth.sweep_workload(hv)
+        p = synth.make(w)
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+
+        def fwd(cp):
+            return gdn.chunk_gated_delta_rule_fwd(
+                d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
+                output_final_state=True, cp_mode=cp, return_states=False)
+
+        def bwd(A, cp):
+            return gdn.chunk_gated_delta_rule_bwd(
+                d["q"], d["k"], d["v"], d["g"], d["beta"], A, d["do"], dht=d["dht"],
+                scale=d["scale"], cp_mode=cp)
+
+        A = fwd(-1)[1]
+        for _ in range(args.warmup):
+            bwd(fwd(-1)[1], -1)
+        rec = {"H_v": hv, "H_q": w.Hq, "T": w.T,
+               "auto_segments_per_head": gdn.plan_segments(d["q"], d["k"], d["v"], cp_mode=-1)}
+        ms = timed(lambda: bwd(fwd(-1)[1], -1), args.steps)
+        rec["step_ms"] = ms
+        rec["step_tokens_per_s"] = w.T / (ms * 1e-3)
+        by_cp = {}
+        for cp in (-1, 0, 4, 8, 13, 16, 26, 32, 64):
+            f = timed(lambda: fwd(cp), max(3, args.steps // 2))
+            b = timed(lambda: bwd(A, cp), max(3, args.steps // 2))
+            by_cp[str(cp)] = {"fwd_ms": round(f, 4), "bwd_ms": round(b, 4)}
+        rec["by_cp_mode"] = by_cp
+        out.append(rec)
+        del d, p
+        torch.cuda.empty_cache()
+    return {"metric": "GDN chunk fwd/bwd head-count sweep (tokens/s per H_v, T=8192)",
+            "unit": "tokens/s", "dtype": "bf16", "data": "synthetic (seeded)",
+            "steps": args.steps, "warmup": args.warmup, "sweep": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +199,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="head-count sweep H_v in 64,48,32,24,16,8 at T=8192 (H_q = H_v/2): "
+                         "fwd / bwd / step times per head count and per context-parallel "
+                         "segment length; prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path; "
@@ -160,6 +222,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": 1 << 30}))
+        return
+
+    if args.sweep:
+        print(json.dumps(sweep(gdn, synth, torch, dev, args)), flush=True)
         return
 
     w = synth.WORKLOADS[args.workload]

@@ -157,6 +157,16 @@ def _contig(x):
     return None if x is None else x.contiguous()
 
 
+def plan_segments(q, k, v, cu_seqlens=None, cp_mode: int = -1) -> int:
+    """Number of context-parallel segments the forward launches for this
+    problem (host-side planning; q, k, v give the shapes only)."""
+    pr = _Prepared(q, v, None, cu_seqlens, cp_mode)
+    n = lib().gdn_plan_segments(pr.ref())
+    if n <= 0:
+        raise ValueError(last_error())
+    return int(n)
+
+
 def _check_inputs(q, k, v, g, beta):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B,T,Hq,K] and v [B,T,Hv,V]")

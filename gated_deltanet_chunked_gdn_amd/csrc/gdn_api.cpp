@@ -7,6 +7,8 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstdint>
 #include <map>
 #include <string>
 #include <vector>
@@ -29,6 +31,26 @@ int fail(int code, const char *fmt, ...) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Compute units of the device the process first plans on (256 on MI355X;
+// also the value used when no device can be queried).  Cached, so that the
+// workspace-size query and the launch always plan alike.
+int64_t device_compute_units() {
+  static std::atomic<int> cached{0};
+  int c = cached.load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      n > 0) {
+    c = n;
+  } else {
+    (void)hipGetLastError();  // leave no error behind for the caller's next HIP call
+    c = 256;
+  }
+  cached.store(c, std::memory_order_relaxed);
+  return c;
+}
 
 bool aligned(const void *ptr, size_t a) {
   return ((uintptr_t)ptr % a) == 0;
@@ -112,10 +134,36 @@ int validate(const gdn_problem_t *p, gdn::Plan *plan) {
   } else if (cp > 0) {
     seg = cp;
   } else {
-    // automatic: about one segment per compute unit, at least 8 chunks long
-    const int64_t work = pl.total_chunks * p->Hv;
-    seg = std::max<int64_t>(8, (work + 255) / 256);
-    seg = std::min<int64_t>(seg, std::max<int64_t>(maxchunks, 1));
+    // automatic: every (segment, v-head) work item of the segment passes
+    // holds one compute unit (its LDS use leaves room for one workgroup), so
+    // a pass takes ceil(items / CUs) rounds of up to `seg` chunk steps each.
+    // Choose the segment length with the least estimated critical path,
+    // rounds x (seg + kItemCost): kItemCost is the fixed cost of one work
+    // item (state load, first-chunk latency, its fix-up item) in chunk steps,
+    // measured along the head-count sweep.  On ties the longer segment wins.
+    // Segments shorter than 4 chunks are not considered.
+    std::vector<int64_t> nc;
+    if (p->cu_seqlens) {
+      for (int n = 0; n < p->N; ++n)
+        nc.push_back((p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n] + 63) / 64);
+    } else {
+      nc.assign(p->B, (p->T + 63) / 64);
+    }
+    const int64_t cus = device_compute_units();
+    seg = std::max<int64_t>(maxchunks, 1);
+    int64_t best_cost = INT64_MAX;
+    for (int64_t sl = std::max<int64_t>(maxchunks, 1); sl >= std::min<int64_t>(4, maxchunks);
+         --sl) {
+      if (sl <= 0) break;
+      int64_t items = 0;
+      for (int64_t c : nc) items += (int64_t)p->Hv * ((c + sl - 1) / sl);
+      constexpr int64_t kItemCost = 6;
+      const int64_t cost = ((items + cus - 1) / cus) * (sl + kItemCost);
+      if (cost < best_cost) {
+        best_cost = cost;
+        seg = sl;
+      }
+    }
   }
   pl.seg_chunks = (int)std::min<int64_t>(seg, 1 << 30);
   pl.total_segs = 0;

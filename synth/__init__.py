@@ -63,6 +63,17 @@ WORKLOADS = {
 }
 
 
+# Head-count sweep of the pages' benchmark (FlashQLA article, "性能基准测试":
+# head counts 64, 48, 32, 24, 16, 8 for TP1..TP8), at the headline length and
+# the headline's q/k grouping (H_q = H_v / 2).
+SWEEP_HV = (64, 48, 32, 24, 16, 8)
+
+
+def sweep_workload(hv: int, T: int = 8192) -> Workload:
+    return Workload(f"sweep_hv{hv}_t{T}", 1, T, hv // 2, hv, 128, 128, "bf16",
+                    backward=True, seed=SEED_BASE + 100 + hv)
+
+
 def _softplus(x):
     return np.logaddexp(0.0, x).astype(np.float32)
 
