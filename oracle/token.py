@@ -18,6 +18,8 @@ import subprocess
 
 import numpy as np
 
+from . import l2norm
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
 _LIB = os.path.join(_HERE, "libgdn_oracle.so")
@@ -104,13 +106,16 @@ def _mask(unit_mask, N, Hv):
 
 
 def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
-        unit_mask=None, threads: int = 0, _lib=None):
+        unit_mask=None, threads: int = 0, qk_l2norm: bool = False, _lib=None):
     """Forward: returns (o [B,T,Hv,V], final_state [N,Hv,K,V]) in float64.
 
     ``unit_mask`` ([N, Hv] bools) restricts the work to selected
     (sequence, v-head) units; other entries of the outputs are zero.
+    ``qk_l2norm`` first L2-normalises every q and k row (``oracle.l2norm``).
     """
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    if qk_l2norm:
+        q, k = l2norm.fwd(q), l2norm.fwd(k)
     h0 = _f64(initial_state)
     B, T, Hq, Hv, K, V, N, cu = _dims(q, v, cu_seqlens)
     if scale is None:
@@ -127,13 +132,19 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
 
 
 def bwd(q, k, v, g, beta, do, dht=None, scale=None, initial_state=None,
-        cu_seqlens=None, unit_mask=None, threads: int = 0, _lib=None):
+        cu_seqlens=None, unit_mask=None, threads: int = 0, qk_l2norm: bool = False,
+        _lib=None):
     """Backward: returns (dq, dk, dv, dbeta, dg, dh0) in float64.
 
     dg is the gradient with respect to the raw log-gate g; dq/dk are summed
-    over the v-heads of each q/k group.
+    over the v-heads of each q/k group.  With ``qk_l2norm`` the recurrence
+    runs on the normalised rows and dq/dk are taken back through the
+    normalisation (with respect to the raw q, k).
     """
     q, k, v, g, beta, do = (_f64(x) for x in (q, k, v, g, beta, do))
+    q_raw, k_raw = q, k
+    if qk_l2norm:
+        q, k = l2norm.fwd(q), l2norm.fwd(k)
     h0 = _f64(initial_state)
     dht = _f64(dht)
     B, T, Hq, Hv, K, V, N, cu = _dims(q, v, cu_seqlens)
@@ -152,4 +163,6 @@ def bwd(q, k, v, g, beta, do, dht=None, scale=None, initial_state=None,
                                 _ptr(db), _ptr(dg), _ptr(dh0), _ptr(m), int(threads))
     if rc != 0:
         raise ValueError(f"oracle bwd rejected the problem (code {rc})")
+    if qk_l2norm:
+        dq, dk = l2norm.bwd(q_raw, dq), l2norm.bwd(k_raw, dk)
     return dq, dk, dv, db, dg, dh0
