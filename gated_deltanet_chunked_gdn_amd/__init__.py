@@ -41,7 +41,7 @@ class GdnProblem(ctypes.Structure):
                 ("Hv", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
-                ("cp_mode", ctypes.c_int32)]
+                ("cp_mode", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -125,7 +125,7 @@ def selftest() -> None:
 class _Prepared:
     """Problem descriptor plus the tensors that must outlive the launch."""
 
-    def __init__(self, q, v, scale, cu_seqlens, cp_mode):
+    def __init__(self, q, v, scale, cu_seqlens, cp_mode, qk_l2norm=False):
         B, T, Hq, K = q.shape
         Hv, V = v.shape[2], v.shape[3]
         if q.dtype == torch.bfloat16:
@@ -147,7 +147,7 @@ class _Prepared:
                                float(K ** -0.5 if scale is None else scale),
                                None if self.cu_dev is None else self.cu_dev.data_ptr(),
                                None if self.cu_host is None else self.cu_host.data_ptr(),
-                               int(cp_mode))
+                               int(cp_mode), int(bool(qk_l2norm)))
 
     def ref(self):
         return ctypes.byref(self.prob)
@@ -183,7 +183,8 @@ def _check_inputs(q, k, v, g, beta):
 def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                cu_seqlens=None, output_final_state=True,
                                return_intermediates=True, cp_mode: int = -1,
-                               return_states: bool = True):
+                               return_states: bool = True,
+                               use_qk_l2norm_in_kernel: bool = False):
     """Forward.  Returns (g_cum, A, o, h, final_state).
 
     g_cum is the gate cumsum inside each 64-token chunk [B,T,Hv]; A the
@@ -191,10 +192,12 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     [B,T,Hv,64]; h the state entering every chunk [NC,Hv,K,V].  With
     return_intermediates=False those three are None (inference mode);
     return_states=False drops only h (the backward does not take it).
+    use_qk_l2norm_in_kernel L2-normalises every q and k row in the library
+    (x * (sum x^2 + 1e-6)^-1/2) before use.
     """
     _check_inputs(q, k, v, g, beta)
     q, k, v, g, beta = (_contig(x) for x in (q, k, v, g, beta))
-    pr = _Prepared(q, v, scale, cu_seqlens, cp_mode)
+    pr = _Prepared(q, v, scale, cu_seqlens, cp_mode, use_qk_l2norm_in_kernel)
     B, T, Hq, K = q.shape
     Hv, V = v.shape[2], v.shape[3]
     dev = q.device
@@ -227,23 +230,28 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
-                           output_final_state=False, cu_seqlens=None, cp_mode: int = -1):
+                           output_final_state=False, cu_seqlens=None, cp_mode: int = -1,
+                           use_qk_l2norm_in_kernel: bool = False):
     """Inference forward: returns (o, final_state or None)."""
     _, _, o, _, ht = chunk_gated_delta_rule_fwd(
         q, k, v, g, beta, scale=scale, initial_state=initial_state, cu_seqlens=cu_seqlens,
-        output_final_state=output_final_state, return_intermediates=False, cp_mode=cp_mode)
+        output_final_state=output_final_state, return_intermediates=False, cp_mode=cp_mode,
+        use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
     return o, ht
 
 
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None,
-                               initial_state=None, cu_seqlens=None, cp_mode: int = -1):
+                               initial_state=None, cu_seqlens=None, cp_mode: int = -1,
+                               use_qk_l2norm_in_kernel: bool = False):
     """Backward.  Returns (dq, dk, dv, db, dg, dh0); dg is w.r.t. the raw g.
 
-    A is the forward's A output (or None to recompute it)."""
+    A is the forward's A output (or None to recompute it).  With
+    use_qk_l2norm_in_kernel (as in the forward) dq, dk are with respect to
+    the raw q, k."""
     _check_inputs(q, k, v, g, beta)
     q, k, v, g, beta, do = (_contig(x) for x in (q, k, v, g, beta, do))
     A, dht, h0 = _contig(A), _contig(dht), _contig(initial_state)
-    pr = _Prepared(q, v, scale, cu_seqlens, cp_mode)
+    pr = _Prepared(q, v, scale, cu_seqlens, cp_mode, use_qk_l2norm_in_kernel)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)

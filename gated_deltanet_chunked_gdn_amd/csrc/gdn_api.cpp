@@ -82,6 +82,8 @@ int validate(const gdn_problem_t *p, gdn::Plan *plan) {
                 "128}, (64, 128), (128, 64); fp32: K, V in {32, 64})",
                 p->K, p->V);
   if (!(p->scale == p->scale)) return fail(GDN_ERR_INVALID_ARG, "scale is NaN");
+  if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
+    return fail(GDN_ERR_INVALID_ARG, "qk_l2norm must be 0 or 1 (got %d)", p->qk_l2norm);
   gdn::Plan pl;
   int64_t maxlen = 0;
   if (p->cu_seqlens) {
@@ -203,6 +205,18 @@ gdn::FwdWorkspace fwd_layout(const gdn_problem_t *p, const gdn::Plan &pl, size_t
   off = align256(off + (size_t)pl.total_segs * p->Hv * kv);
   w.flags = off;
   off = align256(off + (size_t)pl.total_segs * p->Hv * 4);
+  if (p->qk_l2norm) {
+    const size_t rows = (size_t)pl.total_tokens * p->Hq;
+    w.l2 = true;
+    w.qn = off;
+    off = align256(off + rows * p->K * es);
+    w.kn = off;
+    off = align256(off + rows * p->K * es);
+    w.rq = off;
+    off = align256(off + rows * 4);
+    w.rk = off;
+    off = align256(off + rows * 4);
+  }
   w.total = off;
   return w;
 }
@@ -369,7 +383,17 @@ int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   a.h_e = nullptr;
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
-  hipError_t e = gdn::launch_fwd(a, static_cast<hipStream_t>(stream));
+  hipError_t e = hipSuccess;
+  if (wl.l2 && pl.total_tokens > 0) {
+    // every kernel then reads the normalised rows
+    e = gdn::launch_l2norm(a.p, pl.total_tokens, q, k, a.ws + wl.qn, a.ws + wl.kn,
+                           reinterpret_cast<float *>(a.ws + wl.rq),
+                           reinterpret_cast<float *>(a.ws + wl.rk),
+                           static_cast<hipStream_t>(stream));
+    a.q = a.ws + wl.qn;
+    a.k = a.ws + wl.kn;
+  }
+  if (e == hipSuccess) e = gdn::launch_fwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return GDN_OK;
@@ -418,7 +442,18 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   a.dh0 = dh0;
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
-  hipError_t e = gdn::launch_bwd(a, static_cast<hipStream_t>(stream));
+  hipError_t e = hipSuccess;
+  if (wl.fwd.l2 && pl.total_tokens > 0) {
+    e = gdn::launch_l2norm(a.p, pl.total_tokens, q, k, a.ws + wl.fwd.qn, a.ws + wl.fwd.kn,
+                           reinterpret_cast<float *>(a.ws + wl.fwd.rq),
+                           reinterpret_cast<float *>(a.ws + wl.fwd.rk),
+                           static_cast<hipStream_t>(stream));
+    a.q = a.ws + wl.fwd.qn;
+    a.k = a.ws + wl.fwd.kn;
+    a.rq = reinterpret_cast<const float *>(a.ws + wl.fwd.rq);
+    a.rk = reinterpret_cast<const float *>(a.ws + wl.fwd.rk);
+  }
+  if (e == hipSuccess) e = gdn::launch_bwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return GDN_OK;

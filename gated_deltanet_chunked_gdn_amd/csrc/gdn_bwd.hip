@@ -458,16 +458,6 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// A 16-byte piece of element type E with every element times s (rounded once).
-template <typename E>
-__device__ __forceinline__ uint4 scale_piece(const uint4 &x, float s) {
-  uint4 r;
-  const E *a = reinterpret_cast<const E *>(&x);
-  E *b = reinterpret_cast<E *>(&r);
-#pragma unroll
-  for (int e = 0; e < 16 / (int)sizeof(E); ++e) b[e] = from_f32<E>(to_f32(a[e]) * s);
-  return r;
-}
 
 // Per-row values of local_grad, kept at the start of its LDS so that their
 // addresses fit the LDS instructions' immediate offsets.
@@ -1053,6 +1043,50 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   }
 #undef QA
 #undef KA
+  // ---- in-library L2 normalisation: dq, dk so far are with respect to the
+  // normalised rows x_hat = x r (held in sQ, sK); back to the raw rows,
+  // dx = r (dx_hat - x_hat <x_hat, dx_hat>), the row dot taken over K (this
+  // wave's columns, then both column halves through LDS)
+  if (a.rq) {
+    relane();
+    f32x4 xq[NCHK], xk[NCHK];
+    float pq[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NCHK; ++m) {
+      xq[m] = M::ld_acc(sQ + 16 * rt * G::LDK + 16 * (ch * NCHK + m), G::LDK, lane);
+      xk[m] = M::ld_acc(sK + 16 * rt * G::LDK + 16 * (ch * NCHK + m), G::LDK, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pq[i] += xq[m][i] * dq[m][i];
+        pk[i] += xk[m][i] * dk[m][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float tq = sum16(pq[i]), tk = sum16(pk[i]);
+      if (lr == 0) {
+        rowp[0][ch][16 * rt + 4 * lg + i] = tq;
+        rowp[1][ch][16 * rt + 4 * lg + i] = tk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 16 * rt + 4 * lg + i;
+      const float tq = rowp[0][0][s] + rowp[0][1][s];
+      const float tk = rowp[1][0][s] + rowp[1][1][s];
+      float fq = 0.f, fk = 0.f;
+      if (s < rows) {
+        fq = a.rq[(tok0 + s) * p.Hq + hq];
+        fk = a.rk[(tok0 + s) * p.Hq + hq];
+      }
+#pragma unroll
+      for (int m = 0; m < NCHK; ++m) {
+        dq[m][i] = fq * (dq[m][i] - xq[m][i] * tq);
+        dk[m][i] = fk * (dk[m][i] - xk[m][i] * tk);
+      }
+    }
+  }
   // ---- dq, dk of the q/k head (sum over its v-heads in order)
 #pragma unroll
   for (int m = 0; m < NCHK; ++m) {

@@ -154,6 +154,17 @@ __device__ __forceinline__ float dot_piece<float>(const uint4 &a, const uint4 &b
   return c;
 }
 
+// A 16-byte piece of element type E with every element times s (rounded once).
+template <typename E>
+__device__ __forceinline__ uint4 scale_piece(const uint4 &x, float s) {
+  uint4 r;
+  const E *a = reinterpret_cast<const E *>(&x);
+  E *b = reinterpret_cast<E *>(&r);
+#pragma unroll
+  for (int e = 0; e < 16 / (int)sizeof(E); ++e) b[e] = from_f32<E>(to_f32(a[e]) * s);
+  return r;
+}
+
 // Store 4 consecutive elements (8 bytes for bf16, 16 for fp32).
 __device__ __forceinline__ void st4(bf16 *p, float a, float b, float c, float d) {
   bf16x4 v;

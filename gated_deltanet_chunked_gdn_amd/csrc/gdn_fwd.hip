@@ -772,4 +772,61 @@ hipError_t launch_fwd_states(const FwdArgs &a, const float *Ain, hipStream_t st)
   return dispatch_kv<false>(a, Ain, st);
 }
 
+// ------------------------------------------------- in-library L2 normalisation
+// Rows of K elements (one token, one q/k head) of q then k: each thread holds
+// one 16-byte piece and the LPR consecutive lanes of a row combine their sums
+// of squares.  x_hat = x r (rounded once to E), r = (sum x^2 + 1e-6)^-1/2.
+template <typename E, int K>
+__global__ __launch_bounds__(256) void l2norm_kernel(const E *__restrict__ q,
+                                                      const E *__restrict__ k, E *qn, E *kn,
+                                                      float *rq, float *rk, int64_t rows) {
+  constexpr int VEC = 16 / (int)sizeof(E);
+  constexpr int LPR = K / VEC;  // lanes per row: 2 .. 16, divides 64
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = t / LPR;
+  const int part = (int)(t % LPR);
+  const bool active = row < 2 * rows;
+  const bool is_k = row >= rows;
+  const int64_t r = is_k ? row - rows : row;
+  const uint32_t off = (uint32_t)part * 16u;
+  uint4 x = make_uint4(0u, 0u, 0u, 0u);
+  if (active)
+    x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>((is_k ? k : q) + r * K) +
+                                         off);
+  float ss = dot_piece<E>(x, x, 0.f);
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+  const float f = 1.0f / __builtin_sqrtf(ss + 1e-6f);
+  if (active) {
+    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>((is_k ? kn : qn) + r * K) + off) =
+        scale_piece<E>(x, f);
+    if (part == 0) (is_k ? rk : rq)[r] = f;
+  }
+}
+
+hipError_t launch_l2norm(const Problem &p, int64_t tokens, const void *q, const void *k,
+                         void *qn, void *kn, float *rq, float *rk, hipStream_t st) {
+  const int64_t rows = tokens * p.Hq;
+  KernelTimer kt("l2norm", st);
+#define GDN_L2(E, KK)                                                                      \
+  if (p.K == KK) {                                                                        \
+    constexpr int LPR = KK * (int)sizeof(E) / 16;                                         \
+    const int64_t threads = 2 * rows * LPR;                                               \
+    l2norm_kernel<E, KK><<<dim3((unsigned)((threads + 255) / 256)), 256, 0, st>>>(          \
+        static_cast<const E *>(q), static_cast<const E *>(k), static_cast<E *>(qn),        \
+        static_cast<E *>(kn), rq, rk, rows);                                              \
+    return hipGetLastError();                                                              \
+  }
+  if (p.dtype == 1) {
+    GDN_L2(bf16, 32)
+    GDN_L2(bf16, 64)
+    GDN_L2(bf16, 128)
+  } else {
+    GDN_L2(float, 32)
+    GDN_L2(float, 64)
+  }
+#undef GDN_L2
+  return hipErrorInvalidValue;
+}
+
 }  // namespace gdn

@@ -30,6 +30,10 @@ struct FwdWorkspace {
   size_t hseg = 0;          // fp32 [NS][Hv][K][V]: segment end states (pass 1)
   size_t eseg = 0;          // fp32 [NS][Hv][K][V]: propagated starts (pass 2)
   size_t flags = 0;         // int32 [NS][Hv]: eseg non-zero
+  // with in-library q/k L2 normalisation (l2 set): normalised rows and factors
+  bool l2 = false;
+  size_t qn = 0, kn = 0;    // element type [B*T][Hq][K]
+  size_t rq = 0, rk = 0;    // fp32 [B*T][Hq]: (sum x^2 + eps)^-1/2
   size_t total = 0;
 };
 
@@ -69,6 +73,9 @@ struct BwdArgs {
   const float *g, *A, *h0, *dht;
   void *dq, *dk, *dv, *dbeta;
   float *dg, *dh0;
+  // set with in-library q/k L2 normalisation (q, k then point at the
+  // normalised rows): per-row factors for the chain rule of dq, dk
+  const float *rq = nullptr, *rk = nullptr;
   char *ws;
   BwdWorkspace wl;
 };
@@ -77,6 +84,9 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 // states only (a.h), no output; T from Ain ([B,T,Hv,64] fp32) when given
 hipError_t launch_fwd_states(const FwdArgs &a, const float *Ain, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+// q_hat, k_hat (element type) and their per-row factors from raw q, k
+hipError_t launch_l2norm(const Problem &p, int64_t tokens, const void *q, const void *k,
+                         void *qn, void *kn, float *rq, float *rk, hipStream_t stream);
 
 // Benchmark timing: while enabled on the calling thread, each KernelTimer
 // scope records a HIP event before and after the kernel launched inside it,

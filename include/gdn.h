@@ -85,6 +85,12 @@ typedef struct {
                                      without a device->host read) */
   int32_t cp_mode; /* intra-GPU context parallelism: -1 automatic, 0 off,
                       n > 0 = split sequences into segments of n chunks */
+  int32_t qk_l2norm; /* 1: every q and k row (one token, one q/k head) is
+                        L2-normalised inside the library before use,
+                        x * (sum x^2 + 1e-6)^-1/2 (the pages state no such
+                        step; it is the plain reading of the upstream q/k
+                        normalisation), and dq, dk are gradients with respect
+                        to the raw q, k.  0: q, k are used as given. */
 } gdn_problem_t;
 
 /* Workspace bytes gdn_chunk_fwd / gdn_chunk_bwd need for this problem

@@ -89,12 +89,13 @@ def torch_dtype(name: str):
 
 def make(w: Workload, gate: str = "default", T: Optional[int] = None,
          lengths=None, with_h0: Optional[bool] = None,
-         with_grads: Optional[bool] = None):
+         with_grads: Optional[bool] = None, normalize_qk: bool = True):
     """Build one problem as a dict of CPU torch tensors.
 
     ``T`` overrides the sequence length (reduced-size variants); ``lengths``
     overrides the varlen draw; ``with_h0``/``with_grads`` override the
-    workload's flags.  Keys: q k v g beta scale cu_seqlens initial_state
+    workload's flags; ``normalize_qk=False`` keeps q, k as raw N(0, 1) draws
+    (inputs for the in-library L2 normalisation).  Keys: q k v g beta scale cu_seqlens initial_state
     do dht, plus ``lengths`` for varlen problems.
     """
     rng = np.random.default_rng(w.seed)
@@ -112,8 +113,10 @@ def make(w: Workload, gate: str = "default", T: Optional[int] = None,
         Ttot = w.T if T is None else T
         N = B
     sn = lambda *shape: rng.standard_normal(shape, dtype=np.float32)
-    q = _l2n(sn(B, Ttot, Hq, K))
-    k = _l2n(sn(B, Ttot, Hq, K))
+    q = sn(B, Ttot, Hq, K)
+    k = sn(B, Ttot, Hq, K)
+    if normalize_qk:
+        q, k = _l2n(q), _l2n(k)
     v = sn(B, Ttot, Hv, V)
     g = -_softplus(sn(B, Ttot, Hv))
     beta = (1.0 / (1.0 + np.exp(-sn(B, Ttot, Hv)))).astype(np.float32)
@@ -146,7 +149,7 @@ def make(w: Workload, gate: str = "default", T: Optional[int] = None,
 
 
 def custom(B, T, Hq, Hv, K, V, dtype="bf16", seed=1, gate="default",
-           lengths=None, h0=False, grads=False):
+           lengths=None, h0=False, grads=False, normalize_qk=True):
     """Arbitrary-shape problem with the same recipe (for edge-case tests)."""
     w = Workload("custom", B, T, Hq, Hv, K, V, dtype, h0=h0, backward=grads, seed=seed)
-    return make(w, gate=gate, lengths=lengths)
+    return make(w, gate=gate, lengths=lengths, normalize_qk=normalize_qk)

@@ -120,6 +120,12 @@ def test_plan_segments_cp_modes():
     assert L.gdn_plan_segments(ctypes.byref(prob(T=65536, Hv=8, Hq=4))) >= 16
 
 
+def test_qk_l2norm_flag():
+    base = ws(prob())
+    assert ws(prob(qk_l2norm=1)) > base     # room for the normalised rows
+    assert ws(prob(qk_l2norm=2)) == 0 and fwd_rc(prob(qk_l2norm=2)) == 1
+
+
 def test_empty_problem_is_valid():
     p = prob(T=0)
     assert ws(p) > 0
