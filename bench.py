@@ -109,7 +109,7 @@ def traffic_from_profile(kernel, workload):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, p, threads_hint=0):
+def cpu_baseline(w, p, threads_hint=0, l2=False):
     """fp64 oracle forward + reverse mode on a sample of whole q/k groups."""
     import numpy as np
     from oracle import token
@@ -120,9 +120,9 @@ def cpu_baseline(w, p, threads_hint=0):
     mask[0, :units] = True
     t0 = time.perf_counter()
     token.fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], scale=p["scale"], unit_mask=mask,
-              threads=nthr)
+              threads=nthr, qk_l2norm=l2)
     token.bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], p["do"], p["dht"], scale=p["scale"],
-              unit_mask=mask, threads=nthr)
+              unit_mask=mask, threads=nthr, qk_l2norm=l2)
     dt = time.perf_counter() - t0
     toks = w.T * units / w.Hv  # token-equivalents of the full-head workload
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(nthr), "kind": "oracle",
@@ -199,6 +199,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--qk-l2norm", action="store_true",
+                    help="raw q, k inputs, L2-normalised inside the library")
     ap.add_argument("--sweep", action="store_true",
                     help="head-count sweep H_v in 64,48,32,24,16,8 at T=8192 (H_q = H_v/2): "
                          "fwd / bwd / step times per head count and per context-parallel "
@@ -229,7 +231,8 @@ def main():
         return
 
     w = synth.WORKLOADS[args.workload]
-    p = synth.make(w, with_grads=True)
+    p = synth.make(w, with_grads=True, normalize_qk=not args.qk_l2norm)
+    l2 = bool(args.qk_l2norm)
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
     torch.cuda.synchronize()
 
@@ -237,13 +240,14 @@ def main():
         return gdn.chunk_gated_delta_rule_fwd(
             d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
             initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
-            output_final_state=True, cp_mode=args.cp, return_states=False)
+            output_final_state=True, cp_mode=args.cp, return_states=False,
+            use_qk_l2norm_in_kernel=l2)
 
     def bwd(A):
         return gdn.chunk_gated_delta_rule_bwd(
             d["q"], d["k"], d["v"], d["g"], d["beta"], A, d["do"], dht=d["dht"],
             scale=d["scale"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
-            cp_mode=args.cp)
+            cp_mode=args.cp, use_qk_l2norm_in_kernel=l2)
 
     def step():
         out = fwd()
@@ -323,7 +327,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
                 "g=-softplus(N(0,1)), beta=sigmoid(N(0,1)), do N(0,1), dht N(0,0.1))",
-        "config": {"workload": w.name + (" fwd only" if args.fwd_only else " fwd+bwd"),
+        "config": {"workload": w.name + (" fwd only" if args.fwd_only else " fwd+bwd")
+                   + (" (q/k L2-normalised in the library)" if l2 else ""),
                    "B": w.B, "T": w.T, "H_q": w.Hq, "H_v": w.Hv, "K": w.K, "V": w.V,
                    "chunk": CHUNK, "cp_mode": args.cp, "state": "fp32"},
         "roofline": roof,
@@ -335,7 +340,7 @@ def main():
         res["step_tflops"] = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
         res["step_pct_mfma_peak"] = 100 * (fl_fwd + fl_bwd) / (ms_step * 1e-3) / peak_mm
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, p)
+        res["cpu_baseline"] = cpu_baseline(w, p, l2=l2)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

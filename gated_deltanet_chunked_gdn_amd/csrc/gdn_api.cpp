@@ -358,9 +358,9 @@ int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   if (pl.total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
     return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(g, 4) || !aligned(h0, 4) || !aligned(ht, 4) || !aligned(A, 4) ||
+      !aligned(g, 4) || !aligned(h0, 4) || !aligned(ht, 4) || !aligned(A, 16) ||
       !aligned(h, 4) || !aligned(g_cum, 4))
-    return fail(GDN_ERR_LAYOUT, "q, k, v, o must be 16-byte aligned; fp32 buffers 4-byte");
+    return fail(GDN_ERR_LAYOUT, "q, k, v, o, A must be 16-byte aligned; fp32 buffers 4-byte");
   const gdn::FwdWorkspace wl = fwd_layout(p, pl, 0);
   if (!workspace || ws_bytes < wl.total)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,

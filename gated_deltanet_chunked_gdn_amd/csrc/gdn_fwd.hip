@@ -253,17 +253,23 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
       put16(TB(3, 0), LD, t3, -1.f);
     }
     wave_sync();
-    // T out, lane = column: element type (internal, chunk-contiguous rows)
-    // and fp32 A (rows at their tokens)
+    // T out, 4 consecutive columns per lane: element type (internal,
+    // chunk-contiguous rows) and fp32 A (rows at their tokens)
     E *tm = tmat + (gid * p.Hv + h) * 64 * 64;
-    const int cb = lane >> 4, cc = lane & 15;
+    float *arow = a.A ? a.A + (tok0 * p.Hv + h) * 64 : nullptr;
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int idx = lane + 64 * it;
+      const int r = idx >> 4, c0 = (idx & 15) * 4;
+      const int rb = r >> 4, cb = c0 >> 4;
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (cb <= rb) {
+        const float *src = sT + (((rb * (rb + 1)) / 2) + cb) * BS + (r & 15) * LD + (c0 & 15);
 #pragma unroll
-    for (int r = 0; r < 64; ++r) {
-      const int rb = r >> 4;
-      const float x = (cb > rb) ? 0.f
-                                : sT[(((rb * (rb + 1)) / 2) + cb) * BS + (r & 15) * LD + cc];
-      tm[r * 64 + lane] = from_f32<E>(x);
-      if (a.A && r < rows) a.A[((tok0 + r) * p.Hv + h) * 64 + lane] = x;
+        for (int e = 0; e < 4; ++e) x[e] = src[e];
+      }
+      st4(tm + r * 64 + c0, x[0], x[1], x[2], x[3]);
+      if (arow && r < rows) st4(arow + (uint32_t)(r * p.Hv * 64 + c0), x[0], x[1], x[2], x[3]);
     }
     if (a.g_cum && lane < rows) a.g_cum[gi] = gam;
     wave_sync();
@@ -275,9 +281,8 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
 // T from a caller-supplied A ([B,T,Hv,64] fp32, chunk rows at their tokens);
 // padded rows of a last partial chunk become identity rows.
 template <typename E>
-__global__ __launch_bounds__(64) void tmat_from_a_kernel(FwdArgs a, const float *Ain) {
+__global__ __launch_bounds__(256) void tmat_from_a_kernel(FwdArgs a, const float *Ain) {
   const Problem &p = a.p;
-  const int lane = threadIdx.x;
   const int h = (int)(blockIdx.x % p.Hv);
   const int64_t gid = blockIdx.x / p.Hv;
   const ChunkLoc cl =
@@ -285,10 +290,21 @@ __global__ __launch_bounds__(64) void tmat_from_a_kernel(FwdArgs a, const float 
   const int64_t tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
   const int rows = min(kChunk, cl.si.len - cl.c * kChunk);
   E *tm = reinterpret_cast<E *>(a.ws + a.wl.tmat) + (gid * p.Hv + h) * 64 * 64;
-  for (int r = 0; r < 64; ++r) {
-    float x = (r == lane) ? 1.f : 0.f;
-    if (r < rows) x = Ain[((tok0 + r) * p.Hv + h) * 64 + lane];
-    tm[r * 64 + lane] = from_f32<E>(x);
+  const float *ab = Ain + (tok0 * p.Hv + h) * 64;  // row r of the chunk at ab + r*Hv*64
+  // 4 consecutive columns per thread (16-byte load, one store); rows past
+  // the chunk end are rows of the identity
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = threadIdx.x + 256 * it;
+    const int r = idx >> 4, c0 = (idx & 15) * 4;
+    f32x4 x;
+    if (r < rows) {
+      x = *reinterpret_cast<const f32x4 *>(ab + (uint32_t)(r * p.Hv * 64 + c0));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (r == c0 + e) ? 1.f : 0.f;
+    }
+    st4(tm + r * 64 + c0, x[0], x[1], x[2], x[3]);
   }
 }
 
@@ -701,7 +717,7 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
   const Plan &pl = a.plan;
   if (Ain) {
     KernelTimer kt("tmat_from_a", st);
-    tmat_from_a_kernel<E><<<dim3((unsigned)(pl.total_chunks * p.Hv)), 64, 0, st>>>(a, Ain);
+    tmat_from_a_kernel<E><<<dim3((unsigned)(pl.total_chunks * p.Hv)), 256, 0, st>>>(a, Ain);
     return;
   }
   using C = PrepCfg<E, K>;

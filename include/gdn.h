@@ -37,7 +37,7 @@
  *   dv          [B, T, Hv, V], dbeta [B, T, Hv]: problem dtype; dg [B,T,Hv] fp32
  * With cu_seqlens, B must be 1, T is the total packed length and sequence n
  * covers tokens [cu[n], cu[n+1]); chunks never cross sequences.
- * Alignment: q, k, v, o (forward) and q, k, v, do, A (backward) 16 bytes;
+ * Alignment: q, k, v, o, A (forward) and q, k, v, do, A (backward) 16 bytes;
  * every other buffer 4 bytes; the workspace 256 bytes.
  *
  * Ownership: every buffer belongs to the caller.  The library allocates no
