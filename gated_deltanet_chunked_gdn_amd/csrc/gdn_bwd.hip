@@ -415,30 +415,35 @@ __global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
 template <typename E, int K, int V>
 struct LocCfg {
   using G = Geo<E, K, V>;
+  // row pitches: 16 bytes of padding (the segment kernels pad 32 bytes, which
+  // this kernel's LDS footprint has no room for)
+  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int LDK = K + PAD;
+  static constexpr int LDC = 64 + PAD;
   static constexpr int VB = (sizeof(E) == 4) ? 32 : (V < 64 ? V : 64);
   static constexpr int NVB = V / VB;
-  static constexpr int LDB = VB + G::PAD;
+  static constexpr int LDB = VB + PAD;
   static constexpr int NCHB = VB / 32;  // V-block column tiles per half
   static constexpr int NCHK = K / 32;   // key column tiles per half
   static constexpr int oQ = 0;
-  static constexpr int oK = oQ + 64 * G::LDK;
-  static constexpr int oT = oK + 64 * G::LDK;
-  static constexpr int oPt = oT + 64 * G::LDC;
+  static constexpr int oK = oQ + 64 * LDK;
+  static constexpr int oT = oK + 64 * LDK;
+  static constexpr int oPt = oT + 64 * LDC;
   // V-block buffers (dead after the V-block loop)
-  static constexpr int oS = oPt + 64 * G::LDC;     // S block [K][LDB]
+  static constexpr int oS = oPt + 64 * LDC;     // S block [K][LDB]
   static constexpr int oD = oS + K * LDB;          // D block [K][LDB]; later dR [64][LDB]
   static constexpr int oDO = oD + (K > 64 ? K : 64) * LDB;  // dO block [64][LDB]
   static constexpr int oDOq = oDO + 64 * LDB;      // dO rows * scale e^gamma
   static constexpr int oRt = oDOq + 64 * LDB;      // R^T [VB][LDC]; later dVn^T
-  static constexpr int oVn = oRt + VB * G::LDC;    // Vn [64][LDB]
+  static constexpr int oVn = oRt + VB * LDC;    // Vn [64][LDB]
   static constexpr int oVnd = oVn + 64 * LDB;      // Vn rows * e^{gamma_L - gamma}
   static constexpr int oDRs = oVnd + 64 * LDB;     // dR rows * (-beta e^gamma)
   static constexpr int oV = oDRs + 64 * LDB;       // V block [64][LDB]
   static constexpr int nE = oV + 64 * LDB;
   // after the V-block loop: dP * E and dKK [64][LDC] reuse the block buffers
   static constexpr int oPE = oS;
-  static constexpr int oKK = oPE + 64 * G::LDC;
-  static_assert(oKK + 64 * G::LDC <= nE, "LDS reuse");
+  static constexpr int oKK = oPE + 64 * LDC;
+  static_assert(oKK + 64 * LDC <= nE, "LDS reuse");
   static constexpr int bytes = nE * (int)sizeof(E);
 };
 
@@ -581,13 +586,13 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         zq = *reinterpret_cast<const uint4 *>(qtile + off);
         zk = *reinterpret_cast<const uint4 *>(ktile + off);
       }
-      *reinterpret_cast<uint4 *>(sQ + r * G::LDK + cv * VEC) = zq;
-      *reinterpret_cast<uint4 *>(sK + r * G::LDK + cv * VEC) = zk;
+      *reinterpret_cast<uint4 *>(sQ + r * C::LDK + cv * VEC) = zq;
+      *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = zk;
     }
   }
   __syncthreads();
-#define QA(ks) M::ld(sQ + ra * G::LDK + (ks) * KS + EPL * lg)
-#define KA(ks) M::ld(sK + ra * G::LDK + (ks) * KS + EPL * lg)
+#define QA(ks) M::ld(sQ + ra * C::LDK + (ks) * KS + EPL * lg)
+#define KA(ks) M::ld(sK + ra * C::LDK + (ks) * KS + EPL * lg)
   // raw Q K^T and (if wanted) K K^T tiles of this wave (fp32); recomputed
   // where needed rather than held across the v-block loop
   auto qk_tiles = [&](f32x4 *qk, f32x4 *kk) {
@@ -602,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
         if (pc0 + cc <= rt) {
-          const auto kb = M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg);
+          const auto kb = M::ld(sK + (16 * (pc0 + cc) + lr) * C::LDK + ks * KS + EPL * lg);
           qk[cc] = M::mma(qa, kb, qk[cc]);
           if (kk) kk[cc] = M::mma(KA(ks), kb, kk[cc]);
         }
@@ -688,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         const int idx = tid + kThreads * m;
         if (idx < 64 * PT) {
           const int r = idx / PT, cv = idx % PT;
-          *reinterpret_cast<uint4 *>(sT + r * G::LDC + cv * VEC) = pf.t[m];
+          *reinterpret_cast<uint4 *>(sT + r * C::LDC + cv * VEC) = pf.t[m];
         }
       }
       if (tid < 64) {
@@ -717,7 +722,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         const int s = 16 * rt + 4 * lg + i;
         pv[i] = (t <= s) ? qk[cc][i] * __builtin_amdgcn_exp2f(gam_s[i] - gt) : 0.f;
       }
-      st4(sPt + t * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
+      st4(sPt + t * C::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
     }
     }
     f32x4 dp[2], da[2];
@@ -800,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           rr[i] = bet_s[i] * (v4[i] - eg_s[i] * ks_[m][i]);
           de_p[i] += scale * o4[i] * qs_[m][i];
         }
-        st4(sRt + vc * G::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
+        st4(sRt + vc * C::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
       }
       }
 #pragma unroll
@@ -822,11 +827,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int ks = 0; ks < NKC; ++ks) {
-          const auto ta = M::ld(sT + ra * G::LDC + ks * KS + EPL * lg);
+          const auto ta = M::ld(sT + ra * C::LDC + ks * KS + EPL * lg);
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
             vn[m] = M::mma(
-                ta, M::ld(sRt + (16 * (ch * NCHB + m) + lr) * G::LDC + ks * KS + EPL * lg),
+                ta, M::ld(sRt + (16 * (ch * NCHB + m) + lr) * C::LDC + ks * KS + EPL * lg),
                 vn[m]);
         }
 #pragma unroll
@@ -858,7 +863,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         for (int m = 0; m < NCHB; ++m) x[m] = zero4();
 #pragma unroll
         for (int ks = 0; ks < NKC; ++ks) {
-          const auto pa = M::ld(sPt + ra * G::LDC + ks * KS + EPL * lg);
+          const auto pa = M::ld(sPt + ra * C::LDC + ks * KS + EPL * lg);
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
             x[m] = M::mma(
@@ -871,7 +876,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           float y[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) y[i] = dec_s[i] * kd[m][i] + scale * x[m][i];
-          st4(sDVnt + vc * G::LDC + 16 * rt + 4 * lg, y[0], y[1], y[2], y[3]);
+          st4(sDVnt + vc * C::LDC + 16 * rt + 4 * lg, y[0], y[1], y[2], y[3]);
         }
       }
       __syncthreads();
@@ -889,11 +894,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       for (int m = 0; m < NCHB; ++m) dr[m] = zero4();
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks) {
-        const auto tta = M::ld_tr(sT + ks * KS * G::LDC + 16 * rt, G::LDC);
+        const auto tta = M::ld_tr(sT + ks * KS * C::LDC + 16 * rt, C::LDC);
 #pragma unroll
         for (int m = 0; m < NCHB; ++m)
           dr[m] = M::mma(
-              tta, M::ld(sDVnt + (16 * (ch * NCHB + m) + lr) * G::LDC + ks * KS + EPL * lg),
+              tta, M::ld(sDVnt + (16 * (ch * NCHB + m) + lr) * C::LDC + ks * KS + EPL * lg),
               dr[m]);
       }
       __syncthreads();  // D block fully consumed before dR overwrites it
@@ -966,8 +971,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 16 * rt + 4 * lg + i;
-        sPE[s * G::LDC + t] = from_f32<E>(pe[i]);
-        sKK[s * G::LDC + t] = from_f32<E>(kkv[i]);
+        sPE[s * C::LDC + t] = from_f32<E>(pe[i]);
+        sKK[s * C::LDC + t] = from_f32<E>(kkv[i]);
       }
       cs += __shfl_xor(cs, 16, 64);
       cs += __shfl_xor(cs, 32, 64);
@@ -995,14 +1000,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     // ---- phase 8: dq += (dP*E) K;  dk += (dP*E)^T Q + (dKK + dKK^T) K
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
-      const auto pea = M::ld(sPE + ra * G::LDC + ks * KS + EPL * lg);
-      const auto peta = M::ld_tr(sPE + ks * KS * G::LDC + 16 * rt, G::LDC);
-      const auto ma = M::ld_sym_tr(sKK + ra * G::LDC + ks * KS + EPL * lg,
-                                   sKK + ks * KS * G::LDC + 16 * rt, G::LDC);
+      const auto pea = M::ld(sPE + ra * C::LDC + ks * KS + EPL * lg);
+      const auto peta = M::ld_tr(sPE + ks * KS * C::LDC + 16 * rt, C::LDC);
+      const auto ma = M::ld_sym_tr(sKK + ra * C::LDC + ks * KS + EPL * lg,
+                                   sKK + ks * KS * C::LDC + 16 * rt, C::LDC);
 #pragma unroll
       for (int m = 0; m < NCHK; ++m) {
-        const auto kb = M::ld_tr(sK + ks * KS * G::LDK + 16 * (ch * NCHK + m), G::LDK);
-        const auto qb = M::ld_tr(sQ + ks * KS * G::LDK + 16 * (ch * NCHK + m), G::LDK);
+        const auto kb = M::ld_tr(sK + ks * KS * C::LDK + 16 * (ch * NCHK + m), C::LDK);
+        const auto qb = M::ld_tr(sQ + ks * KS * C::LDK + 16 * (ch * NCHK + m), C::LDK);
         dq[m] = M::mma(pea, kb, dq[m]);
         dk[m] = M::mma(peta, qb, dk[m]);
         dk[m] = M::mma(ma, kb, dk[m]);
@@ -1053,8 +1058,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     float pq[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < NCHK; ++m) {
-      xq[m] = M::ld_acc(sQ + 16 * rt * G::LDK + 16 * (ch * NCHK + m), G::LDK, lane);
-      xk[m] = M::ld_acc(sK + 16 * rt * G::LDK + 16 * (ch * NCHK + m), G::LDK, lane);
+      xq[m] = M::ld_acc(sQ + 16 * rt * C::LDK + 16 * (ch * NCHK + m), C::LDK, lane);
+      xk[m] = M::ld_acc(sK + 16 * rt * C::LDK + 16 * (ch * NCHK + m), C::LDK, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pq[i] += xq[m][i] * dq[m][i];

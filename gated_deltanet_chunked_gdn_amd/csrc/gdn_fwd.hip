@@ -67,7 +67,7 @@ __global__ void plan_kernel(Problem p, int seg_chunks, int32_t *chunk_prefix,
 //                    (i - j = 1, 2, 3) as 16x16x16 fp32 MFMA products.
 template <typename E, int K>
 struct PrepCfg {
-  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int PAD = 32 / (int)sizeof(E);  // conflict-free 16-byte fragment reads
   static constexpr int LDK = K + PAD;
   static constexpr int LDA = 68;                          // fp32 64x64 rows
   static constexpr int bytesK = 64 * LDK * (int)sizeof(E);
@@ -449,24 +449,40 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       qs[c2] = zero4();
       kss[c2] = zero4();
     }
+    // Fragments are double-buffered over the k-steps (the reads of step
+    // ks + 1 are issued before the products of step ks).  The two Q K^T tiles
+    // are formed whether or not they lie below the diagonal (P masks them),
+    // which keeps the step free of branches.
+    {
+      typename M::frag fq[2], fk[2], fb[2][NCH], fkb[2][2];
+      auto load_step = [&](int ks, int sl) {
+        fq[sl] = M::ld(sQ + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
+        fk[sl] = M::ld(sK + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
 #pragma unroll
-    for (int ks = 0; ks < NKK; ++ks) {
-      const auto qa = M::ld(sQ + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
-      const auto ka = M::ld(sK + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
+        for (int c2 = 0; c2 < NCH; ++c2)
+          fb[sl][c2] = M::ld(sSt + (16 * (ct0 + c2) + lr) * G::LDK + ks * KS + EPL * lg);
+        if (WRITE_O) {
 #pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2) {
-        const auto b = M::ld(sSt + (16 * (ct0 + c2) + lr) * G::LDK + ks * KS + EPL * lg);
-        // the output is built transposed (rows v, columns r): each lane then
-        // holds 4 consecutive values of one output row
-        if (WRITE_O) qs[c2] = M::mma(b, qa, qs[c2]);
-        kss[c2] = M::mma(ka, b, kss[c2]);
-      }
-      if (WRITE_O) {
+          for (int cc = 0; cc < 2; ++cc)
+            fkb[sl][cc] = M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg);
+        }
+      };
+      load_step(0, 0);
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          if (pc0 + cc <= rt)
-            qk[cc] = M::mma(
-                qa, M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg), qk[cc]);
+      for (int ks = 0; ks < NKK; ++ks) {
+        const int sl = ks & 1;
+        if (ks + 1 < NKK) load_step(ks + 1, sl ^ 1);
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) {
+          // the output is built transposed (rows v, columns r): each lane
+          // then holds 4 consecutive values of one output row
+          if (WRITE_O) qs[c2] = M::mma(fb[sl][c2], fq[sl], qs[c2]);
+          kss[c2] = M::mma(fk[sl], fb[sl][c2], kss[c2]);
+        }
+        if (WRITE_O) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) qk[cc] = M::mma(fq[sl], fkb[sl][cc], qk[cc]);
+        }
       }
     }
     float eg_r[4], b_r[4];

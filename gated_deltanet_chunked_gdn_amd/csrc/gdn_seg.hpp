@@ -112,7 +112,10 @@ __device__ __forceinline__ SegLoc locate_sequence(const Problem &p, int seg_chun
 // Tile geometry of the segment kernels.
 template <typename E, int K, int V>
 struct Geo {
-  static constexpr int PAD = 16 / (int)sizeof(E);
+  // 32 bytes of row padding: 16-byte fragment reads of 16 consecutive rows
+  // are then free of LDS bank conflicts (measured; 16 bytes of padding
+  // leaves half of the LDS cycles to conflicts)
+  static constexpr int PAD = 32 / (int)sizeof(E);
   static constexpr int LDK = K + PAD;   // rows of length K
   static constexpr int LDV = V + PAD;   // rows of length V
   static constexpr int LDC = 64 + PAD;  // rows of length 64 (chunk)
