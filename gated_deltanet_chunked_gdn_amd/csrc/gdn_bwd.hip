@@ -166,33 +166,42 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
                                si.tok0 + (int64_t)c1 * kChunk,
                                min(kChunk, si.len - c1 * kChunk), h, chunk_gid0 + c1, tid);
     }
-    // ---- phase A: K D (rows of tile rt, half of V); P^T
-    typename M::frag ka[NKK];
-#pragma unroll
-    for (int ks = 0; ks < NKK; ++ks)
-      ka[ks] = M::ld(sK + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
+    // ---- phase A: K D (rows of tile rt, half of V); P^T.  Fragments are
+    // double-buffered over the k-steps; the two Q K^T tiles are formed
+    // whether or not they lie below the diagonal (the mask below zeroes them).
+    const int pc0 = 2 * (w >> 2);
     f32x4 kd[NCH];
+    f32x4 qk[2] = {zero4(), zero4()};
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) kd[c2] = zero4();
+    {
+      typename M::frag fk[2], fq[2], fd[2][NCH], fkb[2][2];
+      auto load_step = [&](int ks, int sl) {
+        fk[sl] = M::ld(sK + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
 #pragma unroll
-    for (int ks = 0; ks < NKK; ++ks)
+        for (int c2 = 0; c2 < NCH; ++c2)
+          fd[sl][c2] = M::ld(sDt + (16 * (ct0 + c2) + lr) * G::LDK + ks * KS + EPL * lg);
+        if (MAIN) {
+          fq[sl] = M::ld(sQ + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
 #pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2)
-        kd[c2] = M::mma(ka[ks],
-                        M::ld(sDt + (16 * (ct0 + c2) + lr) * G::LDK + ks * KS + EPL * lg),
-                        kd[c2]);
-    if (MAIN) {
-      const int pc0 = 2 * (w >> 2);
-      f32x4 qk[2] = {zero4(), zero4()};
+          for (int cc = 0; cc < 2; ++cc)
+            fkb[sl][cc] = M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg);
+        }
+      };
+      load_step(0, 0);
 #pragma unroll
       for (int ks = 0; ks < NKK; ++ks) {
-        const auto qa = M::ld(sQ + (16 * rt + lr) * G::LDK + ks * KS + EPL * lg);
+        const int sl = ks & 1;
+        if (ks + 1 < NKK) load_step(ks + 1, sl ^ 1);
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          if (pc0 + cc <= rt)
-            qk[cc] = M::mma(
-                qa, M::ld(sK + (16 * (pc0 + cc) + lr) * G::LDK + ks * KS + EPL * lg), qk[cc]);
+        for (int c2 = 0; c2 < NCH; ++c2) kd[c2] = M::mma(fk[sl], fd[sl][c2], kd[c2]);
+        if (MAIN) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) qk[cc] = M::mma(fq[sl], fkb[sl][cc], qk[cc]);
+        }
       }
+    }
+    if (MAIN) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int t = 16 * (pc0 + cc) + lr;

@@ -511,14 +511,18 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
         st4(sPt + j * G::LDC + 16 * rt + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
       }
     }
+    // V at this lane's accumulator positions (all reads issued first)
+    f32x4 vv[NCH];
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2)
+      vv[c2] =
+          WANT_V ? M::ld_acc(sV + 16 * rt * G::LDV + 16 * (ct0 + c2), G::LDV, lane) : zero4();
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) {
       const int vc = 16 * (ct0 + c2) + lr;
-      const f32x4 vv =
-          WANT_V ? M::ld_acc(sV + 16 * rt * G::LDV + 16 * (ct0 + c2), G::LDV, lane) : zero4();
       float rr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rr[i] = b_r[i] * (vv[i] - eg_r[i] * kss[c2][i]);
+      for (int i = 0; i < 4; ++i) rr[i] = b_r[i] * (vv[c2][i] - eg_r[i] * kss[c2][i]);
       st4(sRt + vc * G::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
     }
     __syncthreads();
