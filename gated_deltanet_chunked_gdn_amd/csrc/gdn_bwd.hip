@@ -91,7 +91,7 @@ __device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem 
   }
   if (tid < 64) {
     const float gam = wave_incl_scan(pf.g) * kLog2e;
-    const float gL = __shfl(gam, 63, 64);
+    const float gL = lane63(gam);
     const float eg = __builtin_amdgcn_exp2f(gam);
     S.gate.gam[tid] = gam;
     S.gate.eg[tid] = eg;
@@ -456,23 +456,6 @@ struct LocCfg {
   static constexpr int bytes = nE * (int)sizeof(E);
 };
 
-// x moved across lanes by a DPP control (rows of 16 lanes)
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-// Sum over the 16 lanes of each DPP row (the lanes that share l >> 4): swap
-// neighbours and pairs inside quads, then rotate the row by 4 and by 8.
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp<0x124>(x);  // row_ror:4
-  x += dpp<0x128>(x);  // row_ror:8
-  return x;
-}
-
-
 // Per-row values of local_grad, kept at the start of its LDS so that their
 // addresses fit the LDS instructions' immediate offsets.
 struct LocSmall {
@@ -584,22 +567,6 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     return *reinterpret_cast<const f32x4 *>(arr + 16 * rt + 4 * lg);
   };
 
-  // ---- chunk tiles of q and k (shared by the group's v-heads)
-  {
-    constexpr int PK = K / VEC;
-    for (int idx = tid; idx < 64 * PK; idx += kThreads) {
-      const int r = idx / PK, cv = idx % PK;
-      uint4 zq = make_uint4(0u, 0u, 0u, 0u), zk = zq;
-      if (r < rows) {
-        const uint32_t off = r * qk_rs + cv * 16u;
-        zq = *reinterpret_cast<const uint4 *>(qtile + off);
-        zk = *reinterpret_cast<const uint4 *>(ktile + off);
-      }
-      *reinterpret_cast<uint4 *>(sQ + r * C::LDK + cv * VEC) = zq;
-      *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = zk;
-    }
-  }
-  __syncthreads();
 #define QA(ks) M::ld(sQ + ra * C::LDK + (ks) * KS + EPL * lg)
 #define KA(ks) M::ld(sK + ra * C::LDK + (ks) * KS + EPL * lg)
   // raw Q K^T and (if wanted) K K^T tiles of this wave (fp32); recomputed
@@ -690,6 +657,36 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   };
   load_head(0);
   load_block(0, 0);
+  // ---- chunk tiles of q and k (shared by the group's v-heads), loaded
+  // together with the first v-head's inputs so that the workgroup waits for
+  // one round trip to memory
+  {
+    constexpr int PK = K / VEC;
+    constexpr int NQP = (64 * PK + kThreads - 1) / kThreads;
+    uint4 zq[NQP], zk[NQP];
+#pragma unroll
+    for (int m = 0; m < NQP; ++m) {
+      const int idx = tid + kThreads * m;
+      const int r = idx / PK, cv = idx % PK;
+      zq[m] = make_uint4(0u, 0u, 0u, 0u);
+      zk[m] = zq[m];
+      if (idx < 64 * PK && r < rows) {
+        const uint32_t off = r * qk_rs + cv * 16u;
+        zq[m] = *reinterpret_cast<const uint4 *>(qtile + off);
+        zk[m] = *reinterpret_cast<const uint4 *>(ktile + off);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NQP; ++m) {
+      const int idx = tid + kThreads * m;
+      if (idx < 64 * PK) {
+        const int r = idx / PK, cv = idx % PK;
+        *reinterpret_cast<uint4 *>(sQ + r * C::LDK + cv * VEC) = zq[m];
+        *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = zk[m];
+      }
+    }
+  }
+  __syncthreads();
 
   for (int hl = 0; hl < Gq; ++hl) {
     relane();
@@ -707,7 +704,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
       if (tid < 64) {
         const float gam = wave_incl_scan(pf.g) * kLog2e;
-        const float gL = __shfl(gam, 63, 64);
+        const float gL = lane63(gam);
         sgam[tid] = gam;
         seg[tid] = __builtin_amdgcn_exp2f(gam);
         sdec[tid] = __builtin_amdgcn_exp2f(gL - gam);
@@ -924,15 +921,23 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           sDR[s * LDB + vc] = from_f32<E>(x);
           // dk += (-beta e^g dR) S^T takes dR with its rows scaled
           sDRs[s * LDB + vc] = from_f32<E>(-bet_s[i] * eg_s[i] * x);
-          if (s < rows)
-            *reinterpret_cast<E *>(dvtile + s * v_rs + (uint32_t)((v0 + vc) * sizeof(E))) =
-                from_f32<E>(bet_s[i] * x);
+          // dv = beta dR replaces this lane's own V elements (read above)
+          sV[s * LDB + vc] = from_f32<E>(bet_s[i] * x);
           db_p[i] += x * (v4[i] - eg_s[i] * ks_[m][i]);
           de_p[i] -= bet_s[i] * x * ks_[m][i];
         }
       }
       }
       __syncthreads();
+      // dv rows of this block, 16 bytes a lane
+#pragma unroll
+      for (int m = 0; m < LP::NOP; ++m) {
+        const int idx = tid + kThreads * m;
+        const int r = idx / PB, cv = idx % PB;
+        if (idx < 64 * PB && r < rows)
+          *reinterpret_cast<uint4 *>(dvtile + r * v_rs + (uint32_t)((v0 + cv * VEC) * sizeof(E))) =
+              *reinterpret_cast<const uint4 *>(sV + r * LDB + cv * VEC);
+      }
       // ---- phase 6: dP += dO Vn^T, dA -= dR Vn^T, dk += (-beta e^g dR) S^T
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
@@ -1000,9 +1005,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
     }
     {
-      float gsum = gl_p;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) gsum += __shfl_xor(gsum, o, 64);
+      const float gsum = wave_sum(gl_p);
       if (lane == 0) glp[w] = gsum;
     }
     __syncthreads();
@@ -1023,13 +1026,12 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);  // bound the gathers in flight
       }
     }
-    // ---- phase 9: dbeta, dgamma -> dg (reverse cumsum inside the chunk)
+    // ---- phase 9: dbeta, dgamma -> dg (reverse cumsum inside the chunk):
+    // lane l takes row 63 - l, so the reverse sum is a prefix sum over lanes
     if (w == 0) {
-      const int r = lane;
+      const int r = 63 - lane;
       const float cr = rowp[3][0][r] + rowp[3][1][r];
-      float csum = cr;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) csum += __shfl_xor(csum, o, 64);
+      const float csum = wave_sum(cr);
       float gl = 0.f;
 #pragma unroll
       for (int i = 0; i < kNW; ++i) gl += glp[i];
@@ -1040,13 +1042,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       float dgam = seg[r] * de + rs - cs - cr;
       if (r == rows - 1) dgam += csum + seg[63] * gl;
       if (r >= rows) dgam = 0.f;
-      // reverse inclusive scan: dg_r = sum_{r' >= r} dgam_r'
-      float x = dgam;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_down(x, d, 64);
-        if (r + d < 64) x += y;
-      }
+      const float x = wave_incl_scan(dgam);  // dg_r = sum_{r' >= r} dgam_r'
       if (r < rows) {
         const int64_t gi = (tok0 + r) * p.Hv + h;
         a.dg[gi] = x;
@@ -1101,17 +1097,34 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
     }
   }
-  // ---- dq, dk of the q/k head (sum over its v-heads in order)
+  // ---- dq, dk of the q/k head (sum over its v-heads in order): each lane
+  // puts its own elements in place of the q, k elements it alone still
+  // reads, then the rows leave 16 bytes a lane
 #pragma unroll
   for (int m = 0; m < NCHK; ++m) {
     const int ic = 16 * (ch * NCHK + m) + lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 16 * rt + 4 * lg + i;
-      if (s < rows) {
-        const int64_t off = ((tok0 + s) * p.Hq + hq) * K + ic;
-        dqp[off] = from_f32<E>(dq[m][i]);
-        dkp[off] = from_f32<E>(dk[m][i]);
+      sQ[s * C::LDK + ic] = from_f32<E>(dq[m][i]);
+      sK[s * C::LDK + ic] = from_f32<E>(dk[m][i]);
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int PK = K / VEC;
+    char *dqtile = reinterpret_cast<char *>(dqp + (tok0 * p.Hq + hq) * K);
+    char *dktile = reinterpret_cast<char *>(dkp + (tok0 * p.Hq + hq) * K);
+#pragma unroll
+    for (int m = 0; m < (64 * PK + kThreads - 1) / kThreads; ++m) {
+      const int idx = tid + kThreads * m;
+      const int r = idx / PK, cv = idx % PK;
+      if (idx < 64 * PK && r < rows) {
+        const uint32_t off = r * qk_rs + cv * 16u;
+        *reinterpret_cast<uint4 *>(dqtile + off) =
+            *reinterpret_cast<const uint4 *>(sQ + r * C::LDK + cv * VEC);
+        *reinterpret_cast<uint4 *>(dktile + off) =
+            *reinterpret_cast<const uint4 *>(sK + r * C::LDK + cv * VEC);
       }
     }
   }

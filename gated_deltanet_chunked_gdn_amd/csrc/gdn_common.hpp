@@ -195,16 +195,43 @@ __device__ __forceinline__ int wave_of(int tid) {
   return __builtin_amdgcn_readfirstlane(tid >> 6);
 }
 
-// Inclusive prefix sum across the 64 lanes of a wavefront.
+// x moved across lanes by a DPP control; lanes that the control gives no
+// source lane, and lanes of rows (16 lanes each) outside ROWS, read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, false));
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront, in registers:
+// shifts by 1, 2, 4 and 8 lanes inside each row of 16, then lane 15's row
+// total broadcast into rows 1 and 3 and lane 31's total into rows 2 and 3.
 __device__ __forceinline__ float wave_incl_scan(float x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    float y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  x += dpp_mov<0x111>(x);       // row_shr:1
+  x += dpp_mov<0x112>(x);       // row_shr:2
+  x += dpp_mov<0x114>(x);       // row_shr:4
+  x += dpp_mov<0x118>(x);       // row_shr:8
+  x += dpp_mov<0x142, 0xA>(x);  // row_bcast:15
+  x += dpp_mov<0x143, 0xC>(x);  // row_bcast:31
   return x;
 }
+
+// Sum over the 16 lanes of each row (the lanes that share l >> 4): swap
+// neighbours and pairs inside quads, then rotate the row by 4 and by 8.
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x124>(x);  // row_ror:4
+  x += dpp_mov<0x128>(x);  // row_ror:8
+  return x;
+}
+
+// Lane 63's value of x, as a wave-uniform float.
+__device__ __forceinline__ float lane63(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+// Sum over all 64 lanes (wave-uniform).
+__device__ __forceinline__ float wave_sum(float x) { return lane63(wave_incl_scan(x)); }
 
 // Locate sequence n with prefix[n] <= x < prefix[n+1] (prefix non-decreasing,
 // prefix[0] = 0, x < prefix[N]).  Skips empty sequences.

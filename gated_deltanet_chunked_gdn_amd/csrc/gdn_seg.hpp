@@ -224,7 +224,7 @@ __device__ __forceinline__ void gate_commit(float g, float b, const GateLds &G,
                                             int tid = threadIdx.x) {
   if (tid < 64) {
     const float gam = wave_incl_scan(g) * kLog2e;
-    const float gL = __shfl(gam, 63, 64);
+    const float gL = lane63(gam);
     G.gam[tid] = gam;
     G.eg[tid] = __builtin_amdgcn_exp2f(gam);
     G.dec[tid] = __builtin_amdgcn_exp2f(gL - gam);
