@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
     if (a.dh0) {
       float *dst = a.dh0 + ((int64_t)n * p.Hv + h) * KV;
       const float *src = a.dht ? a.dht + ((int64_t)n * p.Hv + h) * KV : nullptr;
-      for (int64_t i = threadIdx.x; i < KV; i += blockDim.x) dst[i] = src ? src[i] : 0.f;
+      copy_state<K, V>(dst, src);
     }
     return;
   }
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
     if (a.dh0) {
       float *dst = a.dh0 + ((int64_t)n * p.Hv + h) * KV;
       const float *src = dseg + (sl.seg0 * p.Hv + h) * KV;
-      for (int64_t i = threadIdx.x; i < KV; i += blockDim.x) dst[i] = src[i];
+      copy_state<K, V>(dst, src);
     }
     return;
   }

@@ -77,7 +77,9 @@ struct PrepCfg {
   // blocks transposed with row stride 20 (float4 reads)
   static constexpr int BS = 16 * 17;
   static constexpr int fA = 0, fT = 6 * BS, fM = 16 * BS, fAd = 17 * BS;
-  static constexpr int floatsW = fAd + 4 * 16 * 20;
+  // gamma log2(e) and beta of the chunk rows
+  static constexpr int fG = fAd + 4 * 16 * 20, fB = fG + 64;
+  static constexpr int floatsW = fB + 64;
   static constexpr int bytesW = floatsW * 4;
 };
 
@@ -124,15 +126,40 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
   const int64_t tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
   const int rows = min(kChunk, cl.si.len - cl.c * kChunk);
 
+  // raw gate and beta of this wave's next v-head, loaded one v-head ahead
+  // (the first together with the k tile)
+  float gv_n = 0.f, bv_n = 0.f;
+  auto load_gb = [&](int hl) {
+    gv_n = 0.f;
+    bv_n = 0.f;
+    if (hl < G && lane < rows) {
+      const int64_t gi = (tok0 + lane) * p.Hv + hq * G + hl;
+      gv_n = a.g[gi];
+      bv_n = to_f32(reinterpret_cast<const E *>(a.beta)[gi]);
+    }
+  };
+  load_gb(w);
   const E *kp = reinterpret_cast<const E *>(a.k);
   constexpr int VEC = 16 / (int)sizeof(E);
   constexpr int PR = K / VEC;
-  for (int idx = tid; idx < 64 * PR; idx += blockDim.x) {
-    const int r = idx / PR, cv = idx % PR;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rows)
-      val = *reinterpret_cast<const uint4 *>(kp + ((tok0 + r) * p.Hq + hq) * K + cv * VEC);
-    *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = val;
+  {
+    // every load in flight before the first LDS store (1 or 2 waves)
+    constexpr int NP = PR;  // pieces per thread for one wave
+    uint4 val[NP];
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int idx = tid + (int)blockDim.x * m;
+      const int r = idx / PR, cv = idx % PR;
+      val[m] = make_uint4(0u, 0u, 0u, 0u);
+      if (idx < 64 * PR && r < rows)
+        val[m] = *reinterpret_cast<const uint4 *>(kp + ((tok0 + r) * p.Hq + hq) * K + cv * VEC);
+    }
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int idx = tid + (int)blockDim.x * m;
+      const int r = idx / PR, cv = idx % PR;
+      if (idx < 64 * PR) *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = val[m];
+    }
   }
   __syncthreads();
   const int lr = lane & 15, lg = lane >> 4;
@@ -167,10 +194,13 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
   for (int hl = w; hl < G; hl += nw) {
     const int h = hq * G + hl;
     const int64_t gi = (tok0 + lane) * p.Hv + h;
-    const float gv = lane < rows ? a.g[gi] : 0.f;
-    const float bv = lane < rows ? to_f32(reinterpret_cast<const E *>(a.beta)[gi]) : 0.f;
+    const float gv = gv_n, bv = bv_n;
+    load_gb(hl + nw);
     const float gam = wave_incl_scan(gv);
-    const float gam2 = gam * kLog2e;
+    float *sG = W + C::fG, *sB = W + C::fB;
+    sG[lane] = gam * kLog2e;
+    sB[lane] = bv;
+    wave_sync();
     // A = strict_lower(beta_r exp(gamma_r - gamma_j) KK): off-diagonal blocks
     // row-major, diagonal blocks transposed
     {
@@ -180,13 +210,14 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
 #pragma unroll
         for (int ct = 0; ct <= rt; ++ct, ++t) {
           const int j = 16 * ct + lr;
-          const float gj = __shfl(gam2, j, 64);
+          const float gj = sG[j];
+          const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(sG + 16 * rt + 4 * lg);
+          const f32x4 br4 = *reinterpret_cast<const f32x4 *>(sB + 16 * rt + 4 * lg);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * lg + i;
-            const float gr = __shfl(gam2, r, 64);
-            const float br = __shfl(bv, r, 64);
-            const float val = (j < r) ? br * __builtin_amdgcn_exp2f(gr - gj) * kk[t][i] : 0.f;
+            const float val =
+                (j < r) ? br4[i] * __builtin_amdgcn_exp2f(gr4[i] - gj) * kk[t][i] : 0.f;
             if (ct == rt)
               sAd[(rt * 16 + lr) * 20 + 4 * lg + i] = val;
             else
@@ -685,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void serial_kernel(FwdArgs a) {
     if (a.ht) {
       float *dst = a.ht + ((int64_t)n * p.Hv + h) * KV;
       const float *src = a.h0 ? a.h0 + ((int64_t)n * p.Hv + h) * KV : nullptr;
-      for (int64_t i = threadIdx.x; i < KV; i += blockDim.x) dst[i] = src ? src[i] : 0.f;
+      copy_state<K, V>(dst, src);
     }
     return;
   }
@@ -702,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void serial_kernel(FwdArgs a) {
     if (a.ht) {
       float *dst = a.ht + ((int64_t)n * p.Hv + h) * KV;
       const float *src = hseg + (last * p.Hv + h) * KV;
-      for (int64_t i = threadIdx.x; i < KV; i += blockDim.x) dst[i] = src[i];
+      copy_state<K, V>(dst, src);
     }
     return;
   }

@@ -310,6 +310,44 @@ __device__ __forceinline__ void tiles_store_e(const Tiles<Geo<E, K, V>::NTS> &s,
   }
 }
 
+// dst[0 .. K V) = src[0 .. K V), or zeros when src is null (fp32 states;
+// kThreads threads).  Every load is in flight before the first store: 16
+// bytes a lane when both pointers allow it, else 4.
+template <int K, int V>
+__device__ __forceinline__ void copy_state(float *dst, const float *src) {
+  constexpr int N4 = K * V / 4;
+  constexpr int NP = (N4 + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x;
+  if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15) == 0) {
+    f32x4 x[NP];
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int i = tid + kThreads * m;
+      x[m] = (src && i < N4) ? reinterpret_cast<const f32x4 *>(src)[i] : zero4();
+    }
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int i = tid + kThreads * m;
+      if (i < N4) reinterpret_cast<f32x4 *>(dst)[i] = x[m];
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float x[NP];
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const int i = tid + kThreads * (m + NP * b);
+        x[m] = (src && i < K * V) ? src[i] : 0.f;
+      }
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const int i = tid + kThreads * (m + NP * b);
+        if (i < K * V) dst[i] = x[m];
+      }
+    }
+  }
+}
+
 // Transposed working copy (element type) in LDS: dstT[v][i] = S[i][v].
 template <typename E, int K, int V>
 __device__ __forceinline__ void tiles_to_lds_t(const Tiles<Geo<E, K, V>::NTS> &s, E *dstT,
