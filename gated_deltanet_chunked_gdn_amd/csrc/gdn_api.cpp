@@ -168,6 +168,7 @@ int validate(const gdn_problem_t *p, gdn::Plan *plan) {
     }
   }
   pl.seg_chunks = (int)std::min<int64_t>(seg, 1 << 30);
+  pl.cus = (int)device_compute_units();
   pl.total_segs = 0;
   pl.max_segs_per_seq = 0;
   auto add_seq = [&](int64_t len) {

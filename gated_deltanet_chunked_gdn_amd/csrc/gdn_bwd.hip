@@ -468,6 +468,14 @@ struct LocSmall {
   float glp[kNW];
 };
 
+// One work item of local_grad: chunk gid (global id) of q/k head hq.
+struct LocItem {
+  int hq;
+  int64_t gid;
+  int64_t tok0;
+  int rows;
+};
+
 // Registers that carry the next V block (S, D, dO, V pieces) and, at a v-head
 // boundary, the next v-head's T piece and raw g, beta while the current block
 // is computed.
@@ -534,14 +542,21 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     ra = 16 * rt + lr;
   };
   relane();
-  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int hq = (int)(wid % p.Hq);
-  const int64_t gid = wid / p.Hq;
   const int Gq = p.Hv / p.Hq;
-  const ChunkLoc cl =
-      locate_chunk(p, reinterpret_cast<const int32_t *>(a.ws + a.wl.fwd.chunk_prefix), gid);
-  const int64_t tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
-  const int rows = min(kChunk, cl.si.len - cl.c * kChunk);
+  // Work items are (chunk, q/k head) pairs; a workgroup takes items
+  // blockIdx.x, + gridDim.x, ...  and loads the next item's q, k, first T,
+  // gates and V block while it finishes the current one.
+  const int64_t n_items = a.plan.total_chunks * p.Hq;
+  auto item_of = [&](int64_t it) {
+    LocItem x;
+    x.hq = (int)(it % p.Hq);
+    x.gid = it / p.Hq;
+    const ChunkLoc cl =
+        locate_chunk(p, reinterpret_cast<const int32_t *>(a.ws + a.wl.fwd.chunk_prefix), x.gid);
+    x.tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
+    x.rows = min(kChunk, cl.si.len - cl.c * kChunk);
+    return x;
+  };
   const float scale = p.scale;
   const E *qp = reinterpret_cast<const E *>(a.q);
   const E *kp = reinterpret_cast<const E *>(a.k);
@@ -560,8 +575,6 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   // byte offsets per lane: row strides of q/k and of v/do/dv in bytes.
   const uint32_t qk_rs = (uint32_t)(p.Hq * K * sizeof(E));
   const uint32_t v_rs = (uint32_t)(p.Hv * V * sizeof(E));
-  const char *qtile = reinterpret_cast<const char *>(qp + (tok0 * p.Hq + hq) * K);
-  const char *ktile = reinterpret_cast<const char *>(kp + (tok0 * p.Hq + hq) * K);
   // 4 per-row values of this lane's accumulator rows 16 rt + 4 lg + i
   auto row4 = [&](const float *arr) {
     return *reinterpret_cast<const f32x4 *>(arr + 16 * rt + 4 * lg);
@@ -591,19 +604,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   };
   // dq, dk of the q/k head: every term is accumulated in place
   f32x4 dq[NCHK], dk[NCHK];
-#pragma unroll
-  for (int m = 0; m < NCHK; ++m) {
-    dq[m] = zero4();
-    dk[m] = zero4();
-  }
 
   using LP = LocPref<E, K, V>;
   constexpr int PB = LP::PB;
   LP pf;
   // global loads of V block vb of v-head hl (rows past the chunk end read 0)
-  auto load_block = [&](int hl, int vb) {
-    const int h = hq * Gq + hl;
-    const int64_t cg = gid * p.Hv + h;
+  auto load_block = [&](const LocItem &x, int hl, int vb) {
+    const int h = x.hq * Gq + hl;
+    const int64_t cg = x.gid * p.Hv + h;
     const int v0 = vb * VB;
     const char *hsb = reinterpret_cast<const char *>(hst + cg * (int64_t)K * V + v0);
     const char *dsb = reinterpret_cast<const char *>(dst + cg * (int64_t)K * V + v0);
@@ -620,14 +628,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       pf.s[m] = zs;
       pf.d[m] = zd;
     }
-    const char *vb_ = reinterpret_cast<const char *>(vp + (tok0 * p.Hv + h) * V + v0);
-    const char *ob_ = reinterpret_cast<const char *>(dop + (tok0 * p.Hv + h) * V + v0);
+    const char *vb_ = reinterpret_cast<const char *>(vp + (x.tok0 * p.Hv + h) * V + v0);
+    const char *ob_ = reinterpret_cast<const char *>(dop + (x.tok0 * p.Hv + h) * V + v0);
 #pragma unroll
     for (int m = 0; m < LP::NOP; ++m) {
       const int idx = tid + kThreads * m;
       const int r = idx / PB, cv = idx % PB;
       uint4 zo = make_uint4(0u, 0u, 0u, 0u), zv = zo;
-      if (idx < 64 * PB && r < rows) {
+      if (idx < 64 * PB && r < x.rows) {
         const uint32_t off = r * v_rs + (uint32_t)(cv * 16);
         zo = *reinterpret_cast<const uint4 *>(ob_ + off);
         zv = *reinterpret_cast<const uint4 *>(vb_ + off);
@@ -637,9 +645,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     }
   };
   // global loads of v-head hl's T and raw gates
-  auto load_head = [&](int hl) {
-    const int h = hq * Gq + hl;
-    const int64_t cg = gid * p.Hv + h;
+  auto load_head = [&](const LocItem &x, int hl) {
+    const int h = x.hq * Gq + hl;
+    const int64_t cg = x.gid * p.Hv + h;
     const char *tm = reinterpret_cast<const char *>(tmat + cg * 64 * 64);
 #pragma unroll
     for (int m = 0; m < LP::NTP; ++m) {
@@ -649,42 +657,58 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     }
     pf.g = 0.f;
     pf.b = from_f32<E>(0.f);
-    if (tid < rows) {
-      const int64_t gi = (tok0 + tid) * p.Hv + h;
+    if (tid < x.rows) {
+      const int64_t gi = (x.tok0 + tid) * p.Hv + h;
       pf.g = a.g[gi];
       pf.b = bp[gi];
     }
   };
-  load_head(0);
-  load_block(0, 0);
-  // ---- chunk tiles of q and k (shared by the group's v-heads), loaded
-  // together with the first v-head's inputs so that the workgroup waits for
-  // one round trip to memory
-  {
-    constexpr int PK = K / VEC;
-    constexpr int NQP = (64 * PK + kThreads - 1) / kThreads;
-    uint4 zq[NQP], zk[NQP];
+  // q and k tiles of an item (shared by its v-heads) into registers
+  constexpr int PK = K / VEC;
+  constexpr int NQP = (64 * PK + kThreads - 1) / kThreads;
+  uint4 zq[NQP], zk[NQP];
+  auto load_qk = [&](const LocItem &x) {
+    const char *qtile = reinterpret_cast<const char *>(qp + (x.tok0 * p.Hq + x.hq) * K);
+    const char *ktile = reinterpret_cast<const char *>(kp + (x.tok0 * p.Hq + x.hq) * K);
 #pragma unroll
     for (int m = 0; m < NQP; ++m) {
       const int idx = tid + kThreads * m;
       const int r = idx / PK, cv = idx % PK;
       zq[m] = make_uint4(0u, 0u, 0u, 0u);
       zk[m] = zq[m];
-      if (idx < 64 * PK && r < rows) {
+      if (idx < 64 * PK && r < x.rows) {
         const uint32_t off = r * qk_rs + cv * 16u;
         zq[m] = *reinterpret_cast<const uint4 *>(qtile + off);
         zk[m] = *reinterpret_cast<const uint4 *>(ktile + off);
       }
     }
+  };
+  if (blockIdx.x >= n_items) return;
+  LocItem cur = item_of(blockIdx.x);
+  load_head(cur, 0);
+  load_block(cur, 0, 0);
+  load_qk(cur);
+
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+  relane();
+  const int64_t it_next = it + gridDim.x;
+  const bool has_next = it_next < n_items;
+  const int hq = cur.hq;
+  const int64_t tok0 = cur.tok0;
+  const int rows = cur.rows;
 #pragma unroll
-    for (int m = 0; m < NQP; ++m) {
-      const int idx = tid + kThreads * m;
-      if (idx < 64 * PK) {
-        const int r = idx / PK, cv = idx % PK;
-        *reinterpret_cast<uint4 *>(sQ + r * C::LDK + cv * VEC) = zq[m];
-        *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = zk[m];
-      }
+  for (int m = 0; m < NQP; ++m) {
+    const int idx = tid + kThreads * m;
+    if (idx < 64 * PK) {
+      const int r = idx / PK, cv = idx % PK;
+      *reinterpret_cast<uint4 *>(sQ + r * C::LDK + cv * VEC) = zq[m];
+      *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = zk[m];
     }
+  }
+#pragma unroll
+  for (int m = 0; m < NCHK; ++m) {
+    dq[m] = zero4();
+    dk[m] = zero4();
   }
   __syncthreads();
 
@@ -773,10 +797,14 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       // the next block (and at a v-head boundary the next T and gates) is
       // loaded while this one is computed
       if (vb + 1 < C::NVB) {
-        load_block(hl, vb + 1);
+        load_block(cur, hl, vb + 1);
       } else if (hl + 1 < Gq) {
-        load_head(hl + 1);
-        load_block(hl + 1, 0);
+        load_head(cur, hl + 1);
+        load_block(cur, hl + 1, 0);
+      } else if (has_next) {  // the next item's first v-head
+        const LocItem nxt = item_of(it_next);
+        load_head(nxt, 0);
+        load_block(nxt, 0, 0);
       }
       __syncthreads();
       // ---- phase 2: K S, Q S; R; dq += (scale e^g dO) S^T
@@ -958,6 +986,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
     }
     __syncthreads();  // the block buffers are free: dP*E and dKK reuse them
+    if (hl + 1 == Gq && has_next) load_qk(item_of(it_next));
     // ---- phase 7: masks, dP*E, dKK, dgamma row/column terms
     float rs_p[4] = {0.f, 0.f, 0.f, 0.f};
     f32x4 qk[2], kk[2];
@@ -1128,6 +1157,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
     }
   }
+  __syncthreads();  // sQ, sK read out before the next item's tiles land
+  if (has_next) cur = item_of(it_next);
+  }
 }
 
 // ---------------------------------------------------------------- launch
@@ -1172,7 +1204,11 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   }
   if (pl.total_chunks > 0) {
     KernelTimer kt("local_grad", st);
-    local_grad_kernel<E, K, V><<<dim3((unsigned)(pl.total_chunks * p.Hq)), kThreads, 0, st>>>(a);
+    // persistent: one workgroup per compute unit (its LDS use leaves room
+    // for one), each looping over items
+    const int64_t items = pl.total_chunks * p.Hq;
+    const int64_t grid = std::min<int64_t>(items, pl.cus > 0 ? pl.cus : 256);
+    local_grad_kernel<E, K, V><<<dim3((unsigned)grid), kThreads, 0, st>>>(a);
   }
   return hipGetLastError();
 }

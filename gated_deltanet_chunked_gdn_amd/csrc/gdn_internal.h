@@ -20,6 +20,7 @@ struct Plan {
   int max_segs_per_seq = 0;
   bool has_empty = false;   // some sequence has no tokens
   int64_t total_tokens = 0;
+  int cus = 256;            // compute units of the device
 };
 
 // Byte offsets of the pieces of a workspace (all 256-byte aligned).
