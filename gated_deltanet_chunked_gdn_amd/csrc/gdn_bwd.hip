@@ -157,7 +157,11 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
     const int lr = lane & 15, lg = lane >> 4;
     {
       E *ds = dstates + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
-      tiles_store_e<E, K, V>(st, ds, MODE == kRFix, tid);
+      // (transposed; the pass-1 gradient is the LDS mirror written last step)
+      if (MODE == kRFix)
+        tiles_accumulate_t<E, K, V>(st, ds, tid);
+      else
+        mirror_store_t<E, K, V>(sDt, ds, tid);
     }
     // the previous chunk's inputs travel while this whole chunk is computed
     if (c - 1 >= c_begin) {
@@ -434,14 +438,15 @@ struct LocCfg {
   static constexpr int LDB = VB + PAD;
   static constexpr int NCHB = VB / 32;  // V-block column tiles per half
   static constexpr int NCHK = K / 32;   // key column tiles per half
+  static constexpr int LDSK = K + PAD;  // rows of the transposed S and D blocks
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + 64 * LDK;
   static constexpr int oT = oK + 64 * LDK;
   static constexpr int oPt = oT + 64 * LDC;
   // V-block buffers (dead after the V-block loop)
-  static constexpr int oS = oPt + 64 * LDC;     // S block [K][LDB]
-  static constexpr int oD = oS + K * LDB;          // D block [K][LDB]; later dR [64][LDB]
-  static constexpr int oDO = oD + (K > 64 ? K : 64) * LDB;  // dO block [64][LDB]
+  static constexpr int oS = oPt + 64 * LDC;     // S^T block [VB][LDSK]
+  static constexpr int oD = oS + VB * LDSK;     // D^T block [VB][LDSK]; later dR [64][LDB]
+  static constexpr int oDO = oD + (VB * LDSK > 64 * LDB ? VB * LDSK : 64 * LDB);  // dO block [64][LDB]
   static constexpr int oDOq = oDO + 64 * LDB;      // dO rows * scale e^gamma
   static constexpr int oRt = oDOq + 64 * LDB;      // R^T [VB][LDC]; later dVn^T
   static constexpr int oVn = oRt + VB * LDC;    // Vn [64][LDB]
@@ -483,7 +488,8 @@ template <typename E, int K, int V>
 struct LocPref {
   using C = LocCfg<E, K, V>;
   static constexpr int PB = C::VB * (int)sizeof(E) / 16;  // 16-byte pieces per block row
-  static constexpr int NSP = (K * PB + kThreads - 1) / kThreads;
+  static constexpr int PK = K * (int)sizeof(E) / 16;  // 16-byte pieces per row of S^T, D^T
+  static constexpr int NSP = (C::VB * PK + kThreads - 1) / kThreads;
   static constexpr int NOP = (64 * PB + kThreads - 1) / kThreads;
   static constexpr int NTP = (64 * 64 * (int)sizeof(E) / 16 + kThreads - 1) / kThreads;
   uint4 s[NSP], d[NSP], o[NOP], v[NOP], t[NTP];
@@ -613,15 +619,15 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     const int h = x.hq * Gq + hl;
     const int64_t cg = x.gid * p.Hv + h;
     const int v0 = vb * VB;
-    const char *hsb = reinterpret_cast<const char *>(hst + cg * (int64_t)K * V + v0);
-    const char *dsb = reinterpret_cast<const char *>(dst + cg * (int64_t)K * V + v0);
+    // rows v0 .. v0 + VB - 1 of the transposed states: one contiguous block
+    const char *hsb = reinterpret_cast<const char *>(hst + cg * (int64_t)K * V + v0 * K);
+    const char *dsb = reinterpret_cast<const char *>(dst + cg * (int64_t)K * V + v0 * K);
 #pragma unroll
     for (int m = 0; m < LP::NSP; ++m) {
       const int idx = tid + kThreads * m;
-      const int i = idx / PB, cv = idx % PB;
       uint4 zs = make_uint4(0u, 0u, 0u, 0u), zd = zs;
-      if (idx < K * PB) {
-        const uint32_t off = (uint32_t)((i * V + cv * VEC) * sizeof(E));
+      if (idx < VB * LP::PK) {
+        const uint32_t off = (uint32_t)idx * 16u;
         zs = *reinterpret_cast<const uint4 *>(hsb + off);
         zd = *reinterpret_cast<const uint4 *>(dsb + off);
       }
@@ -774,11 +780,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < LP::NSP; ++m) {
           const int idx = tid + kThreads * m;
-          if (idx < K * PB) {
-            const int i = idx / PB, cv = idx % PB;
+          if (idx < VB * LP::PK) {
+            const int r = idx / LP::PK, cv = idx % LP::PK;
             gl_p = dot_piece<E>(pf.s[m], pf.d[m], gl_p);
-            *reinterpret_cast<uint4 *>(sS + i * LDB + cv * VEC) = pf.s[m];
-            *reinterpret_cast<uint4 *>(sD + i * LDB + cv * VEC) = pf.d[m];
+            *reinterpret_cast<uint4 *>(sS + r * C::LDSK + cv * VEC) = pf.s[m];
+            *reinterpret_cast<uint4 *>(sD + r * C::LDSK + cv * VEC) = pf.d[m];
           }
         }
 #pragma unroll
@@ -820,7 +826,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < NCHB; ++m) {
           const auto b =
-              M::ld_tr(sS + ks * KS * LDB + 16 * (ch * NCHB + m), LDB);
+              M::ld(sS + (16 * (ch * NCHB + m) + lr) * C::LDSK + ks * KS + EPL * lg);
           ks_[m] = M::mma(ka, b, ks_[m]);
           qs_[m] = M::mma(qa, b, qs_[m]);
         }
@@ -847,7 +853,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         const auto da_ = M::ld(sDOq + ra * LDB + ks * KS + EPL * lg);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
-          dq[m] = M::mma(da_, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+          dq[m] = M::mma(da_, M::ld_tr(sS + ks * KS * C::LDSK + 16 * (ch * NCHK + m), C::LDSK),
                          dq[m]);
       }
       __syncthreads();
@@ -874,7 +880,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
             kd[m] = M::mma(
-                ka, M::ld_tr(sD + ks * KS * LDB + 16 * (ch * NCHB + m), LDB),
+                ka, M::ld(sD + (16 * (ch * NCHB + m) + lr) * C::LDSK + ks * KS + EPL * lg),
                 kd[m]);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -920,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         const auto vna = M::ld(sVnd + ra * LDB + ks * KS + EPL * lg);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
-          dk[m] = M::mma(vna, M::ld(sD + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+          dk[m] = M::mma(vna, M::ld_tr(sD + ks * KS * C::LDSK + 16 * (ch * NCHK + m), C::LDSK),
                          dk[m]);
       }
       f32x4 dr[NCHB];
@@ -981,7 +987,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         const auto drs = M::ld(sDRs + ra * LDB + ks * KS + EPL * lg);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
-          dk[m] = M::mma(drs, M::ld(sS + (16 * (ch * NCHK + m) + lr) * LDB + ks * KS + EPL * lg),
+          dk[m] = M::mma(drs, M::ld_tr(sS + ks * KS * C::LDSK + 16 * (ch * NCHK + m), C::LDSK),
                          dk[m]);
       }
     }

@@ -462,7 +462,11 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
     }
     if (a.h_e) {
       E *hs = reinterpret_cast<E *>(a.h_e) + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
-      tiles_store_e<E, K, V>(st, hs, MODE == kFix, tid);
+      // (transposed; the pass-1 state is the LDS mirror written last step)
+      if (MODE == kFix)
+        tiles_accumulate_t<E, K, V>(st, hs, tid);
+      else
+        mirror_store_t<E, K, V>(sSt, hs, tid);
     }
     // the next chunk's inputs travel while this whole chunk is computed (this
     // chunk's inputs were committed to LDS at the end of the previous one)

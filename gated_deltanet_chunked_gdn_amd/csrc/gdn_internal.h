@@ -40,8 +40,8 @@ struct FwdWorkspace {
 
 struct BwdWorkspace {
   FwdWorkspace fwd;  // forward state recompute (its own pieces)
-  size_t hstates = 0;   // element type [NC][Hv][K][V]: state entering each chunk
-  size_t dstates = 0;   // element type [NC][Hv][K][V]: gradient of the state leaving each chunk
+  size_t hstates = 0;   // element type [NC][Hv][V][K]: state entering each chunk, transposed
+  size_t dstates = 0;   // element type [NC][Hv][V][K]: gradient of the state leaving each chunk, transposed
   size_t dseg = 0;      // fp32 [NS][Hv][K][V]: reverse segment partials
   size_t deseg = 0;     // fp32 [NS][Hv][K][V]
   size_t dflags = 0;    // int32 [NS][Hv]

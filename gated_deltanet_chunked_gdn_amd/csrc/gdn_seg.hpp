@@ -286,11 +286,14 @@ __device__ __forceinline__ void tiles_store(const Tiles<Geo<E, K, V>::NTS> &s, f
   }
 }
 
-// Same as tiles_store for an element-type (bf16 or fp32) destination:
-// dst = tiles (+ dst if accumulate), rounded once to E.
+// The per-chunk states of the backward (element type) are stored
+// transposed, dstT[v][k] = S[k][v]: a lane's 4 accumulator rows are then 4
+// consecutive elements, and the LDS mirror (also transposed) leaves as whole
+// rows.
+//
+// dstT += tiles (fp32 sum, rounded once to E), 4 elements a lane.
 template <typename E, int K, int V>
-__device__ __forceinline__ void tiles_store_e(const Tiles<Geo<E, K, V>::NTS> &s, E *dst,
-                                              bool accumulate,
+__device__ __forceinline__ void tiles_accumulate_t(const Tiles<Geo<E, K, V>::NTS> &s, E *dstT,
     int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
   const int w = wave_of(tid), lane = tid & 63;
@@ -300,12 +303,28 @@ __device__ __forceinline__ void tiles_store_e(const Tiles<Geo<E, K, V>::NTS> &s,
 #pragma unroll
   for (int m = 0; m < G::NTS; ++m) {
     const int ct = G::sct(w) + m;
+    E *d = dstT + (uint32_t)((16 * ct + lr) * K + 16 * rt + 4 * lg);
+    float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t off = (uint32_t)((16 * rt + 4 * lg + i) * V + 16 * ct + lr);
-      float x = s[m][i];
-      if (accumulate) x += to_f32(dst[off]);
-      dst[off] = from_f32<E>(x);
+    for (int i = 0; i < 4; ++i) x[i] = s[m][i] + to_f32(d[i]);
+    st4(d, x[0], x[1], x[2], x[3]);
+  }
+}
+
+// dstT = the transposed LDS mirror srcT ([V][G::LDK]), 16 bytes a lane.  The
+// mirror holds the tiles rounded to E, so this equals storing the tiles.
+template <typename E, int K, int V>
+__device__ __forceinline__ void mirror_store_t(const E *srcT, E *dstT, int tid = threadIdx.x) {
+  using G = Geo<E, K, V>;
+  constexpr int PR = K / G::VEC;  // 16-byte pieces per row
+  constexpr int NP = (V * PR + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int m = 0; m < NP; ++m) {
+    const int idx = tid + kThreads * m;
+    if (idx < V * PR) {
+      const int r = idx / PR, cv = idx % PR;
+      *reinterpret_cast<uint4 *>(dstT + r * K + cv * G::VEC) =
+          *reinterpret_cast<const uint4 *>(srcT + r * G::LDK + cv * G::VEC);
     }
   }
 }
