@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--cp", type=int, default=-1, help="cp_mode (-1 automatic)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-state-cache", action="store_true",
+                    help="the backward recomputes the per-chunk states instead of taking "
+                         "the forward's state cache")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--qk-l2norm", action="store_true",
@@ -236,23 +239,33 @@ def main():
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
     torch.cuda.synchronize()
 
-    def fwd():
+    # training keeps the per-chunk states from the forward for the backward
+    # (one buffer, reused every step like an activation buffer)
+    use_cache = not args.no_state_cache and not args.fwd_only
+    cache = (gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=args.cp)
+             if use_cache else None)
+
+    def fwd(with_cache=use_cache):
         return gdn.chunk_gated_delta_rule_fwd(
             d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
             initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
             output_final_state=True, cp_mode=args.cp, return_states=False,
-            use_qk_l2norm_in_kernel=l2)
+            use_qk_l2norm_in_kernel=l2, state_cache=cache if with_cache else None)
 
-    def bwd(A):
+    def bwd(A, with_cache=use_cache):
         return gdn.chunk_gated_delta_rule_bwd(
             d["q"], d["k"], d["v"], d["g"], d["beta"], A, d["do"], dht=d["dht"],
             scale=d["scale"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
-            cp_mode=args.cp, use_qk_l2norm_in_kernel=l2)
+            cp_mode=args.cp, use_qk_l2norm_in_kernel=l2,
+            state_cache=cache if with_cache else None)
 
     def step():
         out = fwd()
         if not args.fwd_only:
             bwd(out[1])
+
+    def step_recompute():
+        bwd(fwd(False)[1], False)
 
     def timed(fn, n):
         torch.cuda.synchronize()
@@ -268,6 +281,11 @@ def main():
     for _ in range(args.warmup):
         step()
     ms_step = timed(step, args.steps)
+    ms_step_recompute = None
+    if use_cache:
+        for _ in range(2):
+            step_recompute()
+        ms_step_recompute = timed(step_recompute, args.steps)
     ms_fwd = timed(fwd, args.steps)
     if not args.fwd_only:
         A = fwd()[1]
@@ -330,11 +348,15 @@ def main():
         "config": {"workload": w.name + (" fwd only" if args.fwd_only else " fwd+bwd")
                    + (" (q/k L2-normalised in the library)" if l2 else ""),
                    "B": w.B, "T": w.T, "H_q": w.Hq, "H_v": w.Hv, "K": w.K, "V": w.V,
-                   "chunk": CHUNK, "cp_mode": args.cp, "state": "fp32"},
+                   "chunk": CHUNK, "cp_mode": args.cp, "state": "fp32",
+                   "state_cache": use_cache},
         "roofline": roof,
         "fwd": direction(ms_fwd, fl_fwd),
         "kernels_us": {k: round(v[1] / v[0] * 1e3, 2) for k, v in kern.items()},
     }
+    if ms_step_recompute is not None:
+        # the same step with the backward recomputing the per-chunk states
+        res["ms_per_step_recompute_states"] = ms_step_recompute
     if not args.fwd_only:
         res["bwd"] = direction(ms_bwd, fl_bwd)
         res["step_tflops"] = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12

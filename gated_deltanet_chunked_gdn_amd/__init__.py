@@ -70,9 +70,11 @@ def lib():
         L.gdn_chunk_bwd_workspace_size.restype = S
         L.gdn_plan_segments.argtypes = [pp]
         L.gdn_plan_segments.restype = ctypes.c_int64
-        L.gdn_chunk_fwd.argtypes = [pp] + [P] * 11 + [P, S, P]
+        L.gdn_state_cache_size.argtypes = [pp]
+        L.gdn_state_cache_size.restype = S
+        L.gdn_chunk_fwd.argtypes = [pp] + [P] * 12 + [P, S, P]
         L.gdn_chunk_fwd.restype = ctypes.c_int
-        L.gdn_chunk_bwd.argtypes = [pp] + [P] * 15 + [P, S, P]
+        L.gdn_chunk_bwd.argtypes = [pp] + [P] * 16 + [P, S, P]
         L.gdn_chunk_bwd.restype = ctypes.c_int
         L.gdn_timing_enable.argtypes = [ctypes.c_int]
         L.gdn_timing_enable.restype = ctypes.c_int
@@ -167,6 +169,32 @@ def plan_segments(q, k, v, cu_seqlens=None, cp_mode: int = -1) -> int:
     return int(n)
 
 
+def state_cache_empty(q, v, cu_seqlens=None, cp_mode: int = -1):
+    """An uninitialised state cache for this problem: the state entering every
+    chunk, stored transposed in q's dtype ([chunks, Hv, V, K]), for
+    chunk_gated_delta_rule_fwd to fill and chunk_gated_delta_rule_bwd to take
+    instead of recomputing those states (memory for compute: 32 KB per chunk
+    and v-head at K = V = 128 in bf16)."""
+    pr = _Prepared(q, v, None, cu_seqlens, cp_mode)
+    n = lib().gdn_state_cache_size(pr.ref())
+    if n == 0:
+        raise ValueError(last_error())
+    Hv, K, V = v.shape[2], q.shape[3], v.shape[3]
+    es = q.element_size()
+    chunks = max(n // (Hv * K * V * es), 0)
+    return torch.empty(chunks, Hv, V, K, device=q.device, dtype=q.dtype)
+
+
+def _check_cache(cache, q, v):
+    if cache is None:
+        return None
+    if (cache.dtype != q.dtype or cache.dim() != 4 or cache.shape[1] != v.shape[2]
+            or cache.shape[2] != v.shape[3] or cache.shape[3] != q.shape[3]
+            or not cache.is_contiguous() or cache.device != q.device):
+        raise ValueError("state_cache must come from state_cache_empty for this problem")
+    return cache
+
+
 def _check_inputs(q, k, v, g, beta):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B,T,Hq,K] and v [B,T,Hv,V]")
@@ -184,7 +212,8 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                cu_seqlens=None, output_final_state=True,
                                return_intermediates=True, cp_mode: int = -1,
                                return_states: bool = True,
-                               use_qk_l2norm_in_kernel: bool = False):
+                               use_qk_l2norm_in_kernel: bool = False,
+                               state_cache=None):
     """Forward.  Returns (g_cum, A, o, h, final_state).
 
     g_cum is the gate cumsum inside each 64-token chunk [B,T,Hv]; A the
@@ -193,7 +222,8 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     return_intermediates=False those three are None (inference mode);
     return_states=False drops only h (the backward does not take it).
     use_qk_l2norm_in_kernel L2-normalises every q and k row in the library
-    (x * (sum x^2 + 1e-6)^-1/2) before use.
+    (x * (sum x^2 + 1e-6)^-1/2) before use.  state_cache (from
+    state_cache_empty) is filled with the per-chunk states for the backward.
     """
     _check_inputs(q, k, v, g, beta)
     q, k, v, g, beta = (_contig(x) for x in (q, k, v, g, beta))
@@ -223,8 +253,9 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
         raise GdnError(1, last_error())
     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    cache = _check_cache(state_cache, q, v)
     _check(L.gdn_chunk_fwd(pr.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
-                           _ptr(o), _ptr(ht), _ptr(g_cum), _ptr(A), _ptr(h),
+                           _ptr(o), _ptr(ht), _ptr(g_cum), _ptr(A), _ptr(h), _ptr(cache),
                            _ptr(ws), ws_bytes, ctypes.c_void_p(stream)))
     return g_cum, A, o, h, ht
 
@@ -242,12 +273,13 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
 
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None,
                                initial_state=None, cu_seqlens=None, cp_mode: int = -1,
-                               use_qk_l2norm_in_kernel: bool = False):
+                               use_qk_l2norm_in_kernel: bool = False, state_cache=None):
     """Backward.  Returns (dq, dk, dv, db, dg, dh0); dg is w.r.t. the raw g.
 
     A is the forward's A output (or None to recompute it).  With
     use_qk_l2norm_in_kernel (as in the forward) dq, dk are with respect to
-    the raw q, k."""
+    the raw q, k.  state_cache: the cache the forward of the same inputs
+    filled (the per-chunk states are then not recomputed), or None."""
     _check_inputs(q, k, v, g, beta)
     q, k, v, g, beta, do = (_contig(x) for x in (q, k, v, g, beta, do))
     A, dht, h0 = _contig(A), _contig(dht), _contig(initial_state)
@@ -268,6 +300,6 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None,
     stream = torch.cuda.current_stream(dev).cuda_stream
     _check(L.gdn_chunk_bwd(pr.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
                            _ptr(h0), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv),
-                           _ptr(db), _ptr(dg), _ptr(dh0), _ptr(ws), ws_bytes,
-                           ctypes.c_void_p(stream)))
+                           _ptr(db), _ptr(dg), _ptr(dh0), _ptr(_check_cache(state_cache, q, v)),
+                           _ptr(ws), ws_bytes, ctypes.c_void_p(stream)))
     return dq, dk, dv, db, dg, dh0

@@ -342,6 +342,14 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p) {
   return bwd_layout(p, pl).total;
 }
 
+size_t gdn_state_cache_size(const gdn_problem_t *p) {
+  gdn::Plan pl;
+  if (validate(p, &pl) != GDN_OK) return 0;
+  const size_t es = p->dtype == GDN_BF16 ? 2 : 4;
+  const size_t n = (size_t)pl.total_chunks * p->Hv * p->K * p->V * es;
+  return n > 0 ? n : 16;  // a valid size even for an empty problem
+}
+
 int64_t gdn_plan_segments(const gdn_problem_t *p) {
   gdn::Plan pl;
   if (validate(p, &pl) != GDN_OK) return 0;
@@ -350,8 +358,8 @@ int64_t gdn_plan_segments(const gdn_problem_t *p) {
 
 int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
                   const float *g, const void *beta, const float *h0, void *o, float *ht,
-                  float *g_cum, float *A, float *h, void *workspace, size_t ws_bytes,
-                  void *stream) {
+                  float *g_cum, float *A, float *h, void *state_cache, void *workspace,
+                  size_t ws_bytes, void *stream) {
   g_err.clear();
   gdn::Plan pl;
   int rc = validate(p, &pl);
@@ -360,8 +368,9 @@ int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const vo
     return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(g, 4) || !aligned(h0, 4) || !aligned(ht, 4) || !aligned(A, 16) ||
-      !aligned(h, 4) || !aligned(g_cum, 4))
-    return fail(GDN_ERR_LAYOUT, "q, k, v, o, A must be 16-byte aligned; fp32 buffers 4-byte");
+      !aligned(h, 4) || !aligned(g_cum, 4) || !aligned(state_cache, 16))
+    return fail(GDN_ERR_LAYOUT,
+                "q, k, v, o, A, state_cache must be 16-byte aligned; fp32 buffers 4-byte");
   const gdn::FwdWorkspace wl = fwd_layout(p, pl, 0);
   if (!workspace || ws_bytes < wl.total)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
@@ -381,7 +390,7 @@ int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   a.g_cum = g_cum;
   a.A = A;
   a.h = h;
-  a.h_e = nullptr;
+  a.h_e = state_cache;  // the segment passes store the states they run through
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
   hipError_t e = hipSuccess;
@@ -403,8 +412,8 @@ int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const vo
 int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
                   const float *g, const void *beta, const float *A, const float *h0,
                   const void *do_, const float *dht, void *dq, void *dk, void *dv,
-                  void *dbeta, float *dg, float *dh0, void *workspace, size_t ws_bytes,
-                  void *stream) {
+                  void *dbeta, float *dg, float *dh0, const void *state_cache,
+                  void *workspace, size_t ws_bytes, void *stream) {
   g_err.clear();
   gdn::Plan pl;
   int rc = validate(p, &pl);
@@ -416,8 +425,9 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(do_, 16) ||
       !aligned(dq, 4) || !aligned(dk, 4) || !aligned(dv, 4) || !aligned(g, 4) ||
       !aligned(A, 16) || !aligned(h0, 4) || !aligned(dht, 4) || !aligned(dh0, 4) ||
-      !aligned(dg, 4))
-    return fail(GDN_ERR_LAYOUT, "q, k, v, do, A must be 16-byte aligned; fp32 buffers 4-byte");
+      !aligned(dg, 4) || !aligned(state_cache, 16))
+    return fail(GDN_ERR_LAYOUT,
+                "q, k, v, do, A, state_cache must be 16-byte aligned; fp32 buffers 4-byte");
   const gdn::BwdWorkspace wl = bwd_layout(p, pl);
   if (!workspace || ws_bytes < wl.total)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
@@ -441,6 +451,7 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   a.dbeta = dbeta;
   a.dg = dg;
   a.dh0 = dh0;
+  a.hcache = state_cache;
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
   hipError_t e = hipSuccess;

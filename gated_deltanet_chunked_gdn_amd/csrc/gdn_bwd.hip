@@ -570,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   const E *dop = reinterpret_cast<const E *>(a.dout);
   const E *bp = reinterpret_cast<const E *>(a.beta);
   const E *tmat = reinterpret_cast<const E *>(a.ws + a.wl.fwd.tmat);
-  const E *hst = reinterpret_cast<const E *>(a.ws + a.wl.hstates);
+  const E *hst = reinterpret_cast<const E *>(a.hcache ? a.hcache : a.ws + a.wl.hstates);
   const E *dst = reinterpret_cast<const E *>(a.ws + a.wl.dstates);
   E *dqp = reinterpret_cast<E *>(a.dq);
   E *dkp = reinterpret_cast<E *>(a.dk);
@@ -1190,8 +1190,13 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   fa.h_e = a.ws + a.wl.hstates;
   fa.ws = a.ws;
   fa.wl = a.wl.fwd;
-  hipError_t e = launch_fwd_states(fa, a.A, st);
+  // plan and T; then the per-chunk states, unless the forward left them
+  hipError_t e = launch_bwd_prep(fa, a.A, st);
   if (e != hipSuccess) return e;
+  if (!a.hcache) {
+    e = launch_fwd_states(fa, st);
+    if (e != hipSuccess) return e;
+  }
   if (pl.total_chunks > 0) {
     {
       KernelTimer kt("rev_main", st);

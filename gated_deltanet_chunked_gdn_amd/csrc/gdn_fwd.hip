@@ -783,18 +783,25 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
   prep_kernel<E, K><<<dim3((unsigned)(pl.total_chunks * p.Hq)), 64 * nw, lds, st>>>(a);
 }
 
+// Stage bits of launch_fwd_t: the plan prefix sums and prep (T from k or
+// from a given A), then the segment passes.
+constexpr int kStagePrep = 1, kStageSegs = 2;
+
 template <typename E, int K, int V, bool WRITE_O>
-static hipError_t launch_fwd_t(const FwdArgs &a, const float *Ain, hipStream_t st) {
+static hipError_t launch_fwd_t(const FwdArgs &a, const float *Ain, hipStream_t st, int stages) {
   const Problem &p = a.p;
   const Plan &pl = a.plan;
-  if (p.cu) {
-    KernelTimer kt("plan", st);
-    plan_kernel<<<1, 64, 0, st>>>(p, pl.seg_chunks,
-                                  reinterpret_cast<int32_t *>(a.ws + a.wl.chunk_prefix),
-                                  reinterpret_cast<int32_t *>(a.ws + a.wl.seg_prefix));
+  if (stages & kStagePrep) {
+    if (p.cu) {
+      KernelTimer kt("plan", st);
+      plan_kernel<<<1, 64, 0, st>>>(p, pl.seg_chunks,
+                                    reinterpret_cast<int32_t *>(a.ws + a.wl.chunk_prefix),
+                                    reinterpret_cast<int32_t *>(a.ws + a.wl.seg_prefix));
+    }
+    if (pl.total_chunks > 0) launch_prep<E, K>(a, Ain, st);
   }
+  if (!(stages & kStageSegs)) return hipGetLastError();
   if (pl.total_chunks > 0) {
-    launch_prep<E, K>(a, Ain, st);
     {
       KernelTimer kt(WRITE_O ? "fwd_main" : "state_main", st);
       segment_kernel<E, K, V, kMain, WRITE_O>
@@ -814,10 +821,10 @@ static hipError_t launch_fwd_t(const FwdArgs &a, const float *Ain, hipStream_t s
 }
 
 template <bool WRITE_O>
-static hipError_t dispatch_kv(const FwdArgs &a, const float *Ain, hipStream_t st) {
+static hipError_t dispatch_kv(const FwdArgs &a, const float *Ain, hipStream_t st, int stages) {
   const int K = a.p.K, V = a.p.V;
 #define GDN_KV(E, KK, VV) \
-  if (K == KK && V == VV) return launch_fwd_t<E, KK, VV, WRITE_O>(a, Ain, st);
+  if (K == KK && V == VV) return launch_fwd_t<E, KK, VV, WRITE_O>(a, Ain, st, stages);
   if (a.p.dtype == 1) {
     GDN_KV(bf16, 128, 128)
     GDN_KV(bf16, 64, 64)
@@ -835,12 +842,17 @@ static hipError_t dispatch_kv(const FwdArgs &a, const float *Ain, hipStream_t st
 }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st) {
-  return dispatch_kv<true>(a, nullptr, st);
+  return dispatch_kv<true>(a, nullptr, st, kStagePrep | kStageSegs);
 }
 
-// Forward state recompute for the backward: states only (a.h), no output.
-hipError_t launch_fwd_states(const FwdArgs &a, const float *Ain, hipStream_t st) {
-  return dispatch_kv<false>(a, Ain, st);
+// The backward's prep: plan prefix sums and T (from the forward's A if given).
+hipError_t launch_bwd_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
+  return dispatch_kv<false>(a, Ain, st, kStagePrep);
+}
+
+// Forward state recompute for the backward: states only (a.h_e), no output.
+hipError_t launch_fwd_states(const FwdArgs &a, hipStream_t st) {
+  return dispatch_kv<false>(a, nullptr, st, kStageSegs);
 }
 
 // ------------------------------------------------- in-library L2 normalisation

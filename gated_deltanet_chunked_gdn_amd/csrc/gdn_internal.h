@@ -77,13 +77,17 @@ struct BwdArgs {
   // set with in-library q/k L2 normalisation (q, k then point at the
   // normalised rows): per-row factors for the chain rule of dq, dk
   const float *rq = nullptr, *rk = nullptr;
+  // the forward's state cache ([chunks][Hv][V][K], element type), or null:
+  // then the states are recomputed into the workspace
+  const void *hcache = nullptr;
   char *ws;
   BwdWorkspace wl;
 };
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 // states only (a.h), no output; T from Ain ([B,T,Hv,64] fp32) when given
-hipError_t launch_fwd_states(const FwdArgs &a, const float *Ain, hipStream_t stream);
+hipError_t launch_bwd_prep(const FwdArgs &a, const float *Ain, hipStream_t stream);
+hipError_t launch_fwd_states(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 // q_hat, k_hat (element type) and their per-row factors from raw q, k
 hipError_t launch_l2norm(const Problem &p, int64_t tokens, const void *q, const void *k,

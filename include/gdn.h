@@ -37,8 +37,9 @@
  *   dv          [B, T, Hv, V], dbeta [B, T, Hv]: problem dtype; dg [B,T,Hv] fp32
  * With cu_seqlens, B must be 1, T is the total packed length and sequence n
  * covers tokens [cu[n], cu[n+1]); chunks never cross sequences.
- * Alignment: q, k, v, o, A (forward) and q, k, v, do, A (backward) 16 bytes;
- * every other buffer 4 bytes; the workspace 256 bytes.
+ * Alignment: q, k, v, o, A, state_cache (forward) and q, k, v, do, A,
+ * state_cache (backward) 16 bytes; every other buffer 4 bytes; the
+ * workspace 256 bytes.
  *
  * Ownership: every buffer belongs to the caller.  The library allocates no
  * device memory; scratch comes from the caller's workspace (size from the
@@ -98,25 +99,39 @@ typedef struct {
 size_t gdn_chunk_fwd_workspace_size(const gdn_problem_t *p);
 size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p);
 
+/* Bytes of the state cache of this problem (0 if invalid): the state
+ * entering every chunk, in the element type, stored transposed,
+ * [chunks][Hv][V][K] (chunks in token order, sequence by sequence).  It is
+ * an opaque hand-over from gdn_chunk_fwd to gdn_chunk_bwd, the
+ * memory-for-compute trade of training: with it the backward skips its
+ * recompute of these states. */
+size_t gdn_state_cache_size(const gdn_problem_t *p);
+
 /* Forward (chunk_gated_delta_rule_fwd of the FlashQLA article, "底层 API").
  * Required: q k v g beta o.  Optional (NULL = not wanted / absent):
  * h0 (initial state, else zero), ht (final state = output_final_state),
- * g_cum, A, h (per-chunk entering states, the training-mode extras). */
+ * g_cum, A, h (per-chunk entering states, the training-mode extras),
+ * state_cache (gdn_state_cache_size bytes, 16-byte aligned, filled for the
+ * backward). */
 int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k,
                   const void *v, const float *g, const void *beta,
                   const float *h0, void *o, float *ht, float *g_cum, float *A,
-                  float *h, void *workspace, size_t ws_bytes, void *stream);
+                  float *h, void *state_cache, void *workspace, size_t ws_bytes,
+                  void *stream);
 
 /* Backward (chunk_gated_delta_rule_bwd of the same section).  g is the raw
  * log-gate; dg is with respect to it.  A (as written by gdn_chunk_fwd) is
  * optional: NULL recomputes it.  h0 and dht are optional (zero), dh0 is
- * optional output.  Required: q k v g beta do dq dk dv dbeta dg. */
+ * optional output.  state_cache is optional: the cache a gdn_chunk_fwd of
+ * the same problem, inputs and h0 filled (then the per-chunk states are not
+ * recomputed; NULL recomputes them).  Required: q k v g beta do dq dk dv
+ * dbeta dg. */
 int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k,
                   const void *v, const float *g, const void *beta,
                   const float *A, const float *h0, const void *do_,
                   const float *dht, void *dq, void *dk, void *dv, void *dbeta,
-                  float *dg, float *dh0, void *workspace, size_t ws_bytes,
-                  void *stream);
+                  float *dg, float *dh0, const void *state_cache,
+                  void *workspace, size_t ws_bytes, void *stream);
 
 /* Number of context-parallel segments the forward would launch for this
  * problem (host-only planning query; 0 if invalid). */

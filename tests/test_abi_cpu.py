@@ -37,12 +37,12 @@ def ws(p):
     return gdn.lib().gdn_chunk_fwd_workspace_size(ctypes.byref(p))
 
 
-def fwd_rc(p, ptr=16, wsb=1 << 30, workspace=1 << 20, o=None):
+def fwd_rc(p, ptr=16, wsb=1 << 30, workspace=1 << 20, o=None, cache=None):
     L = gdn.lib()
     P = ctypes.c_void_p
     return L.gdn_chunk_fwd(ctypes.byref(p), P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), None,
-                           P(ptr if o is None else o), None, None, None, None, P(workspace),
-                           wsb, None)
+                           P(ptr if o is None else o), None, None, None, None, cache,
+                           P(workspace), wsb, None)
 
 
 def test_valid_problem_sizes():
@@ -88,10 +88,11 @@ def test_null_and_misaligned_pointers_and_workspace():
     L = gdn.lib()
     P = ctypes.c_void_p
     rc = L.gdn_chunk_fwd(ctypes.byref(p), None, P(16), P(16), P(16), P(16), None, P(16),
-                         None, None, None, None, P(1 << 20), 1 << 30, None)
+                         None, None, None, None, None, P(1 << 20), 1 << 30, None)
     assert rc == 1
     assert fwd_rc(p, ptr=18) == 3                 # q not 16-byte aligned
     assert fwd_rc(p, o=20) == 3                   # o written with 8/16-byte stores
+    assert fwd_rc(p, cache=ctypes.c_void_p(24)) == 3  # state cache moved 16 bytes a lane
     assert fwd_rc(p, wsb=16) == 4                  # workspace too small
     assert fwd_rc(p, workspace=0) == 4             # no workspace
     assert fwd_rc(p, workspace=(1 << 20) + 64) == 4  # workspace misaligned
@@ -101,11 +102,11 @@ def test_bwd_validation():
     p = prob(Hq=3)
     L = gdn.lib()
     P = ctypes.c_void_p
-    rc = L.gdn_chunk_bwd(ctypes.byref(p), *([P(16)] * 15), P(1 << 20), 1 << 30, None)
+    rc = L.gdn_chunk_bwd(ctypes.byref(p), *([P(16)] * 16), P(1 << 20), 1 << 30, None)
     assert rc == 2
     p = prob()
     rc = L.gdn_chunk_bwd(ctypes.byref(p), P(16), P(16), P(16), P(16), P(16), None, None,
-                         P(16), None, None, P(16), P(16), P(16), P(16), None,
+                         P(16), None, None, P(16), P(16), P(16), P(16), None, None,
                          P(1 << 20), 1 << 30, None)
     assert rc == 1  # dq missing
 
@@ -124,6 +125,14 @@ def test_qk_l2norm_flag():
     base = ws(prob())
     assert ws(prob(qk_l2norm=1)) > base     # room for the normalised rows
     assert ws(prob(qk_l2norm=2)) == 0 and fwd_rc(prob(qk_l2norm=2)) == 1
+
+
+def test_state_cache_size():
+    L = gdn.lib()
+    p = prob(T=8192, Hv=64, Hq=32)
+    assert L.gdn_state_cache_size(ctypes.byref(p)) == 128 * 64 * 128 * 128 * 2
+    assert L.gdn_state_cache_size(ctypes.byref(prob(T=100))) == 2 * 4 * 128 * 128 * 2
+    assert L.gdn_state_cache_size(ctypes.byref(prob(Hq=3))) == 0
 
 
 def test_empty_problem_is_valid():

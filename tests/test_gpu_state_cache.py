@@ -1,0 +1,82 @@
+"""GPU: the backward with the forward's state cache.
+
+The training-mode forward can leave the state entering every chunk in a
+cache that the backward then takes instead of recomputing those states.  The
+cache path must give the same gradients as the recompute path (the same
+segment passes compute the same states in both) and stay within the oracle
+tolerance, across the passes that write the cache: the main pass, the fix-up
+pass of segments past the first (forced short segments), the serial residual
+pass (gates that do not decay), packed sequences with empty ones, an initial
+state, fp32 and the in-library q/k normalisation.
+"""
+import pytest
+import torch
+
+import synth
+from tests.gpu_util import TOL, announce, oracle_bwd, rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["dq", "dk", "dv", "db", "dg", "dh0"]
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_chunked_gdn_amd as g
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    g.lib()
+    return g
+
+
+def both(gdn, p, cp_mode, l2=False):
+    d = to_dev(p)
+    kw = dict(scale=d["scale"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+              cp_mode=cp_mode, use_qk_l2norm_in_kernel=l2)
+    cache = gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode)
+    cache.fill_(float("nan"))  # every entry must be written by the forward
+    _, A, _, _, _ = gdn.chunk_gated_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                   state_cache=cache, **kw)
+    with_cache = gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], A,
+                                                d["do"], dht=d["dht"], state_cache=cache, **kw)
+    recompute = gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], A,
+                                               d["do"], dht=d["dht"], **kw)
+    torch.cuda.synchronize()
+    assert not torch.isnan(cache).any(), "state cache entries left unwritten"
+    return with_cache, recompute
+
+
+CASES = [
+    # label, builder, dtype, cp_mode, l2
+    ("bf16 T=300 cp=1", lambda: synth.custom(2, 300, 2, 4, 128, 128, dtype="bf16", seed=5,
+                                             gate="slow", h0=True, grads=True), "bf16", 1, False),
+    ("bf16 nodecay cp=1", lambda: synth.custom(1, 600, 2, 4, 64, 128, dtype="bf16", seed=6,
+                                               gate="nodecay", h0=True, grads=True), "bf16", 1,
+     False),
+    ("bf16 varlen+empty cp=2", lambda: synth.custom(1, 0, 2, 4, 128, 128, dtype="bf16", seed=7,
+                                                    gate="default", lengths=[0, 1, 64, 330, 0,
+                                                                             700, 63],
+                                                    h0=True, grads=True), "bf16", 2, False),
+    ("bf16 auto", lambda: synth.custom(1, 1000, 2, 4, 128, 128, dtype="bf16", seed=8,
+                                       gate="default", h0=False, grads=True), "bf16", -1, False),
+    ("f32 cp=1", lambda: synth.custom(1, 200, 1, 3, 64, 32, dtype="f32", seed=9, gate="slow",
+                                      h0=True, grads=True), "f32", 1, False),
+    ("bf16 l2norm cp=1", lambda: synth.custom(1, 260, 2, 4, 128, 128, dtype="bf16", seed=10,
+                                              gate="slow", h0=True, grads=True,
+                                              normalize_qk=False), "bf16", 1, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_cache_matches_recompute_and_oracle(gdn, case):
+    label, build, dtype, cp, l2 = case
+    announce(f"state cache {label}")
+    p = build()
+    got, rec = both(gdn, p, cp, l2)
+    for n, x, y in zip(NAMES, got, rec):
+        # the same passes produce the same states: equal up to rounding order
+        assert rel(x.float().cpu().numpy(), y.float().cpu().numpy()) <= 1e-6, n
+    ref = oracle_bwd(p) if not l2 else None
+    if ref is not None:
+        errs = {n: rel(x, r) for n, x, r in zip(NAMES, got, ref)}
+        bad = {n: e for n, e in errs.items() if not e <= TOL[dtype]}
+        assert not bad, f"{label}: {bad} (all: {errs})"
