@@ -155,14 +155,15 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
   for (int c = c_end - 1; c >= c_begin && !zero_exit; --c) {
     const int tid = opaque_tid(), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
-    {
-      E *ds = dstates + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
-      // (transposed; the pass-1 gradient is the LDS mirror written last step)
-      if (MODE == kRFix)
-        tiles_accumulate_t<E, K, V>(st, ds, tid);
-      else
-        mirror_store_t<E, K, V>(sDt, ds, tid);
-    }
+    // per-chunk gradients (transposed): pass 1 stores the LDS mirror written
+    // last step; the fix-up pass adds its correction, reading the stored
+    // values here and writing the sums after phase A
+    E *ds = dstates + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
+    TilesOld<E, K, V> dold;
+    if (MODE == kRFix)
+      tiles_old_t<E, K, V>(dold, ds, tid);
+    else
+      mirror_store_t<E, K, V>(sDt, ds, tid);
     // the previous chunk's inputs travel while this whole chunk is computed
     if (c - 1 >= c_begin) {
       const int c1 = c - 1;
@@ -205,6 +206,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
         }
       }
     }
+    if (MODE == kRFix) tiles_accumulate_t<E, K, V>(st, dold, ds, tid);
     if (MAIN) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {

@@ -291,10 +291,43 @@ __device__ __forceinline__ void tiles_store(const Tiles<Geo<E, K, V>::NTS> &s, f
 // consecutive elements, and the LDS mirror (also transposed) leaves as whole
 // rows.
 //
-// dstT += tiles (fp32 sum, rounded once to E), 4 elements a lane.
+// dstT += tiles (fp32 sum, rounded once to E), 4 elements a lane, in two
+// halves so that the read's latency hides behind other work: the old values
+// are read first (tiles_old_t), added and written back later
+// (tiles_accumulate_t), before the tiles change.
+template <typename E>
+struct E4 {
+  using type = bf16x4;
+};
+template <>
+struct E4<float> {
+  using type = f32x4;
+};
 template <typename E, int K, int V>
-__device__ __forceinline__ void tiles_accumulate_t(const Tiles<Geo<E, K, V>::NTS> &s, E *dstT,
-    int tid = threadIdx.x) {
+struct TilesOld {
+  typename E4<E>::type x[Geo<E, K, V>::NTS];
+};
+
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_old_t(TilesOld<E, K, V> &o, const E *dstT,
+                                            int tid = threadIdx.x) {
+  using G = Geo<E, K, V>;
+  const int w = wave_of(tid), lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  if (!G::owns(w)) return;
+  const int rt = G::srt(w);
+#pragma unroll
+  for (int m = 0; m < G::NTS; ++m) {
+    const int ct = G::sct(w) + m;
+    o.x[m] = *reinterpret_cast<const typename E4<E>::type *>(
+        dstT + (uint32_t)((16 * ct + lr) * K + 16 * rt + 4 * lg));
+  }
+}
+
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_accumulate_t(const Tiles<Geo<E, K, V>::NTS> &s,
+                                                   const TilesOld<E, K, V> &o, E *dstT,
+                                                   int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
   const int w = wave_of(tid), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -304,10 +337,8 @@ __device__ __forceinline__ void tiles_accumulate_t(const Tiles<Geo<E, K, V>::NTS
   for (int m = 0; m < G::NTS; ++m) {
     const int ct = G::sct(w) + m;
     E *d = dstT + (uint32_t)((16 * ct + lr) * K + 16 * rt + 4 * lg);
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = s[m][i] + to_f32(d[i]);
-    st4(d, x[0], x[1], x[2], x[3]);
+    st4(d, s[m][0] + to_f32(o.x[m][0]), s[m][1] + to_f32(o.x[m][1]),
+        s[m][2] + to_f32(o.x[m][2]), s[m][3] + to_f32(o.x[m][3]));
   }
 }
 
