@@ -170,26 +170,23 @@ def plan_segments(q, k, v, cu_seqlens=None, cp_mode: int = -1) -> int:
 
 
 def state_cache_empty(q, v, cu_seqlens=None, cp_mode: int = -1):
-    """An uninitialised state cache for this problem: the state entering every
-    chunk, stored transposed in q's dtype ([chunks, Hv, V, K]), for
-    chunk_gated_delta_rule_fwd to fill and chunk_gated_delta_rule_bwd to take
-    instead of recomputing those states (memory for compute: 32 KB per chunk
-    and v-head at K = V = 128 in bf16)."""
+    """An uninitialised state cache for this problem (an opaque uint8 buffer):
+    chunk_gated_delta_rule_fwd fills it with the state entering every chunk
+    and every chunk's T, and chunk_gated_delta_rule_bwd then takes those
+    instead of recomputing them (memory for compute: 40 KB per chunk and
+    v-head at K = V = 128 in bf16)."""
     pr = _Prepared(q, v, None, cu_seqlens, cp_mode)
     n = lib().gdn_state_cache_size(pr.ref())
     if n == 0:
         raise ValueError(last_error())
-    Hv, K, V = v.shape[2], q.shape[3], v.shape[3]
-    es = q.element_size()
-    chunks = max(n // (Hv * K * V * es), 0)
-    return torch.empty(chunks, Hv, V, K, device=q.device, dtype=q.dtype)
+    return torch.empty(n, device=q.device, dtype=torch.uint8)
 
 
-def _check_cache(cache, q, v):
+def _check_cache(cache, pr, q):
     if cache is None:
         return None
-    if (cache.dtype != q.dtype or cache.dim() != 4 or cache.shape[1] != v.shape[2]
-            or cache.shape[2] != v.shape[3] or cache.shape[3] != q.shape[3]
+    n = lib().gdn_state_cache_size(pr.ref())
+    if (cache.dtype != torch.uint8 or cache.dim() != 1 or cache.numel() < n
             or not cache.is_contiguous() or cache.device != q.device):
         raise ValueError("state_cache must come from state_cache_empty for this problem")
     return cache
@@ -253,7 +250,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
         raise GdnError(1, last_error())
     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    cache = _check_cache(state_cache, q, v)
+    cache = _check_cache(state_cache, pr, q)
     _check(L.gdn_chunk_fwd(pr.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                            _ptr(o), _ptr(ht), _ptr(g_cum), _ptr(A), _ptr(h), _ptr(cache),
                            _ptr(ws), ws_bytes, ctypes.c_void_p(stream)))
@@ -279,7 +276,8 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None,
     A is the forward's A output (or None to recompute it).  With
     use_qk_l2norm_in_kernel (as in the forward) dq, dk are with respect to
     the raw q, k.  state_cache: the cache the forward of the same inputs
-    filled (the per-chunk states are then not recomputed), or None."""
+    filled (the per-chunk states and T are then taken from it and A is not
+    read), or None."""
     _check_inputs(q, k, v, g, beta)
     q, k, v, g, beta, do = (_contig(x) for x in (q, k, v, g, beta, do))
     A, dht, h0 = _contig(A), _contig(dht), _contig(initial_state)
@@ -300,6 +298,6 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None,
     stream = torch.cuda.current_stream(dev).cuda_stream
     _check(L.gdn_chunk_bwd(pr.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
                            _ptr(h0), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv),
-                           _ptr(db), _ptr(dg), _ptr(dh0), _ptr(_check_cache(state_cache, q, v)),
+                           _ptr(db), _ptr(dg), _ptr(dh0), _ptr(_check_cache(state_cache, pr, q)),
                            _ptr(ws), ws_bytes, ctypes.c_void_p(stream)))
     return dq, dk, dv, db, dg, dh0

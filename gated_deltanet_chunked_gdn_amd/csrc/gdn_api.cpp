@@ -342,12 +342,19 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p) {
   return bwd_layout(p, pl).total;
 }
 
+// State cache layout: the per-chunk states ([chunks][Hv][V][K], element
+// type), then at a 256-byte boundary the per-chunk T ([chunks][Hv][64][64]).
+static size_t cache_t_offset(const gdn_problem_t *p, const gdn::Plan &pl) {
+  const size_t es = p->dtype == GDN_BF16 ? 2 : 4;
+  return align256((size_t)pl.total_chunks * p->Hv * p->K * p->V * es);
+}
+
 size_t gdn_state_cache_size(const gdn_problem_t *p) {
   gdn::Plan pl;
   if (validate(p, &pl) != GDN_OK) return 0;
   const size_t es = p->dtype == GDN_BF16 ? 2 : 4;
-  const size_t n = (size_t)pl.total_chunks * p->Hv * p->K * p->V * es;
-  return n > 0 ? n : 16;  // a valid size even for an empty problem
+  const size_t n = cache_t_offset(p, pl) + (size_t)pl.total_chunks * p->Hv * 64 * 64 * es;
+  return n > 0 ? n : 256;  // a valid size even for an empty problem
 }
 
 int64_t gdn_plan_segments(const gdn_problem_t *p) {
@@ -391,6 +398,7 @@ int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   a.A = A;
   a.h = h;
   a.h_e = state_cache;  // the segment passes store the states they run through
+  if (state_cache) a.tm_ext = static_cast<char *>(state_cache) + cache_t_offset(p, pl);
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
   hipError_t e = hipSuccess;
@@ -452,6 +460,7 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   a.dg = dg;
   a.dh0 = dh0;
   a.hcache = state_cache;
+  if (state_cache) a.tm_ext = static_cast<const char *>(state_cache) + cache_t_offset(p, pl);
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
   hipError_t e = hipSuccess;

@@ -137,7 +137,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
   const E *kp = reinterpret_cast<const E *>(a.k);
   const E *dop = reinterpret_cast<const E *>(a.dout);
   const E *bp = reinterpret_cast<const E *>(a.beta);
-  const E *tmat = reinterpret_cast<const E *>(a.ws + a.wl.fwd.tmat);
+  const E *tmat = reinterpret_cast<const E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.fwd.tmat);
   E *dstates = reinterpret_cast<E *>(a.ws + a.wl.dstates);
 
   if (c_begin >= c_end)
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   const E *vp = reinterpret_cast<const E *>(a.v);
   const E *dop = reinterpret_cast<const E *>(a.dout);
   const E *bp = reinterpret_cast<const E *>(a.beta);
-  const E *tmat = reinterpret_cast<const E *>(a.ws + a.wl.fwd.tmat);
+  const E *tmat = reinterpret_cast<const E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.fwd.tmat);
   const E *hst = reinterpret_cast<const E *>(a.hcache ? a.hcache : a.ws + a.wl.hstates);
   const E *dst = reinterpret_cast<const E *>(a.ws + a.wl.dstates);
   E *dqp = reinterpret_cast<E *>(a.dq);
@@ -1190,6 +1190,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   fa.A = nullptr;
   fa.h = nullptr;
   fa.h_e = a.ws + a.wl.hstates;
+  fa.tm_ext = const_cast<void *>(a.tm_ext);
   fa.ws = a.ws;
   fa.wl = a.wl.fwd;
   // plan and T; then the per-chunk states, unless the forward left them

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
   // lower block (i >= j) of T, off-diagonal block (i > j) of A
 #define TB(i, j) (sT + (((i) * ((i) + 1)) / 2 + (j)) * BS)
 #define AB(i, j) (sA + (((i) * ((i) - 1)) / 2 + (j)) * BS)
-  E *tmat = reinterpret_cast<E *>(a.ws + a.wl.tmat);
+  E *tmat = reinterpret_cast<E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat);
   for (int hl = w; hl < G; hl += nw) {
     const int h = hq * G + hl;
     const int64_t gi = (tok0 + lane) * p.Hv + h;
@@ -320,7 +320,8 @@ __global__ __launch_bounds__(256) void tmat_from_a_kernel(FwdArgs a, const float
       locate_chunk(p, reinterpret_cast<const int32_t *>(a.ws + a.wl.chunk_prefix), gid);
   const int64_t tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
   const int rows = min(kChunk, cl.si.len - cl.c * kChunk);
-  E *tm = reinterpret_cast<E *>(a.ws + a.wl.tmat) + (gid * p.Hv + h) * 64 * 64;
+  E *tm = reinterpret_cast<E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat) +
+          (gid * p.Hv + h) * 64 * 64;
   const float *ab = Ain + (tok0 * p.Hv + h) * 64;  // row r of the chunk at ab + r*Hv*64
   // 4 consecutive columns per thread (16-byte load, one store); rows past
   // the chunk end are rows of the identity
@@ -436,7 +437,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
   const E *kp = reinterpret_cast<const E *>(a.k);
   const E *vp = reinterpret_cast<const E *>(a.v);
   const E *bp = reinterpret_cast<const E *>(a.beta);
-  const E *tmat = reinterpret_cast<const E *>(a.ws + a.wl.tmat);
+  const E *tmat = reinterpret_cast<const E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat);
 
   if (c_begin >= c_end)
     return MODE == kFix ? !block_any(tiles_nonzero<E, K, V>(st), S.flag) : false;
@@ -790,21 +791,19 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
 
 // Stage bits of launch_fwd_t: the plan prefix sums and prep (T from k or
 // from a given A), then the segment passes.
-constexpr int kStagePrep = 1, kStageSegs = 2;
+constexpr int kStagePlan = 1, kStageT = 2, kStageSegs = 4;
 
 template <typename E, int K, int V, bool WRITE_O>
 static hipError_t launch_fwd_t(const FwdArgs &a, const float *Ain, hipStream_t st, int stages) {
   const Problem &p = a.p;
   const Plan &pl = a.plan;
-  if (stages & kStagePrep) {
-    if (p.cu) {
-      KernelTimer kt("plan", st);
-      plan_kernel<<<1, 64, 0, st>>>(p, pl.seg_chunks,
-                                    reinterpret_cast<int32_t *>(a.ws + a.wl.chunk_prefix),
-                                    reinterpret_cast<int32_t *>(a.ws + a.wl.seg_prefix));
-    }
-    if (pl.total_chunks > 0) launch_prep<E, K>(a, Ain, st);
+  if ((stages & kStagePlan) && p.cu) {
+    KernelTimer kt("plan", st);
+    plan_kernel<<<1, 64, 0, st>>>(p, pl.seg_chunks,
+                                  reinterpret_cast<int32_t *>(a.ws + a.wl.chunk_prefix),
+                                  reinterpret_cast<int32_t *>(a.ws + a.wl.seg_prefix));
   }
+  if ((stages & kStageT) && pl.total_chunks > 0) launch_prep<E, K>(a, Ain, st);
   if (!(stages & kStageSegs)) return hipGetLastError();
   if (pl.total_chunks > 0) {
     {
@@ -847,12 +846,13 @@ static hipError_t dispatch_kv(const FwdArgs &a, const float *Ain, hipStream_t st
 }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st) {
-  return dispatch_kv<true>(a, nullptr, st, kStagePrep | kStageSegs);
+  return dispatch_kv<true>(a, nullptr, st, kStagePlan | kStageT | kStageSegs);
 }
 
-// The backward's prep: plan prefix sums and T (from the forward's A if given).
+// The backward's prep: plan prefix sums and, unless a state cache holds it,
+// T (from the forward's A if given).
 hipError_t launch_bwd_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
-  return dispatch_kv<false>(a, Ain, st, kStagePrep);
+  return dispatch_kv<false>(a, Ain, st, kStagePlan | (a.tm_ext ? 0 : kStageT));
 }
 
 // Forward state recompute for the backward: states only (a.h_e), no output.

@@ -63,6 +63,7 @@ struct FwdArgs {
   void *o;
   float *ht, *g_cum, *A, *h;
   void *h_e;  // per-chunk states in the element type (backward's internal copy)
+  void *tm_ext = nullptr;  // per-chunk T there instead of the workspace (state cache)
   char *ws;
   FwdWorkspace wl;
 };
@@ -80,6 +81,7 @@ struct BwdArgs {
   // the forward's state cache ([chunks][Hv][V][K], element type), or null:
   // then the states are recomputed into the workspace
   const void *hcache = nullptr;
+  const void *tm_ext = nullptr;  // per-chunk T of the same cache
   char *ws;
   BwdWorkspace wl;
 };

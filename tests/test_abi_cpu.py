@@ -130,8 +130,9 @@ def test_qk_l2norm_flag():
 def test_state_cache_size():
     L = gdn.lib()
     p = prob(T=8192, Hv=64, Hq=32)
-    assert L.gdn_state_cache_size(ctypes.byref(p)) == 128 * 64 * 128 * 128 * 2
-    assert L.gdn_state_cache_size(ctypes.byref(prob(T=100))) == 2 * 4 * 128 * 128 * 2
+    # states, then T at a 256-byte boundary
+    assert L.gdn_state_cache_size(ctypes.byref(p)) == 128 * 64 * (128 * 128 + 64 * 64) * 2
+    assert L.gdn_state_cache_size(ctypes.byref(prob(T=100))) == 2 * 4 * (128 * 128 + 64 * 64) * 2
     assert L.gdn_state_cache_size(ctypes.byref(prob(Hq=3))) == 0
 
 

@@ -33,7 +33,7 @@ def both(gdn, p, cp_mode, l2=False):
     kw = dict(scale=d["scale"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
               cp_mode=cp_mode, use_qk_l2norm_in_kernel=l2)
     cache = gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode)
-    cache.fill_(float("nan"))  # every entry must be written by the forward
+    cache.fill_(255)  # NaN in bf16 and fp32: every entry must be written by the forward
     _, A, _, _, _ = gdn.chunk_gated_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                    state_cache=cache, **kw)
     with_cache = gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], A,
@@ -41,7 +41,23 @@ def both(gdn, p, cp_mode, l2=False):
     recompute = gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], A,
                                                d["do"], dht=d["dht"], **kw)
     torch.cuda.synchronize()
-    assert not torch.isnan(cache).any(), "state cache entries left unwritten"
+    # both parts of the cache written: the states, then (at the next 256-byte
+    # boundary) the per-chunk T
+    es = d["q"].element_size()
+    B, T = d["q"].shape[:2]
+    Hv, K, V = d["v"].shape[2], d["q"].shape[3], d["v"].shape[3]
+    if d["cu_seqlens"] is not None:
+        lens = (d["cu_seqlens"][1:] - d["cu_seqlens"][:-1]).tolist()
+        nc = sum((n + 63) // 64 for n in lens)
+    else:
+        nc = B * ((T + 63) // 64)
+    n_st = nc * Hv * K * V * es
+    t_off = (n_st + 255) // 256 * 256
+    states = cache[:n_st].view(d["q"].dtype)
+    tm = cache[t_off:t_off + nc * Hv * 64 * 64 * es].view(d["q"].dtype)
+    assert cache.numel() == t_off + nc * Hv * 64 * 64 * es
+    assert not torch.isnan(states).any(), "state cache: states left unwritten"
+    assert not torch.isnan(tm).any(), "state cache: T left unwritten"
     return with_cache, recompute
 
 
