@@ -867,13 +867,15 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           vn[m] = zero4();
           kd[m] = zero4();
         }
+        // Vn built transposed (Vn^T = R^T T^T): each lane then holds 4
+        // consecutive columns of row 16 rt + (l & 15)
 #pragma unroll
         for (int ks = 0; ks < NKC; ++ks) {
           const auto ta = M::ld(sT + ra * C::LDC + ks * KS + EPL * lg);
 #pragma unroll
           for (int m = 0; m < NCHB; ++m)
             vn[m] = M::mma(
-                ta, M::ld(sRt + (16 * (ch * NCHB + m) + lr) * C::LDC + ks * KS + EPL * lg),
+                M::ld(sRt + (16 * (ch * NCHB + m) + lr) * C::LDC + ks * KS + EPL * lg), ta,
                 vn[m]);
         }
 #pragma unroll
@@ -888,15 +890,23 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         }
         __syncthreads();  // R^T fully consumed before dVn^T overwrites it
         const f32x4 dec_s = row4(sdec);
+        {
+          const float dec_r = sdec[ra];
 #pragma unroll
-        for (int m = 0; m < NCHB; ++m) {
-          const int vc = 16 * (ch * NCHB + m) + lr;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sVn[(16 * rt + 4 * lg + i) * LDB + vc] = from_f32<E>(vn[m][i]);
+          for (int m = 0; m < NCHB; ++m) {
+            E *o = sVn + ra * LDB + 16 * (ch * NCHB + m) + 4 * lg;
+            st4(o, vn[m][0], vn[m][1], vn[m][2], vn[m][3]);
             // dk += (e^{gL-g} Vn) D^T takes Vn with its rows scaled
-            sVnd[(16 * rt + 4 * lg + i) * LDB + vc] = from_f32<E>(dec_s[i] * vn[m][i]);
-            c_p[i] += dec_s[i] * vn[m][i] * kd[m][i];
+            st4(sVnd + (o - sVn), dec_r * vn[m][0], dec_r * vn[m][1], dec_r * vn[m][2],
+                dec_r * vn[m][3]);
+          }
+          // c_r = e^{gL-g_r} <Vn_r, (K D)_r>: Vn read back at the K D tiles'
+          // accumulator positions (this wave's own tiles)
+#pragma unroll
+          for (int m = 0; m < NCHB; ++m) {
+            const f32x4 v4 = M::ld_acc(sVn + 16 * rt * LDB + 16 * (ch * NCHB + m), LDB, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c_p[i] += dec_s[i] * v4[i] * kd[m][i];
           }
         }
         // ---- phase 4a: dVn = dec * (K D) + scale P^T dO
@@ -1019,12 +1029,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         cs += term;
         db_p[i] += dam * kk[cc][i] * e;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = 16 * rt + 4 * lg + i;
-        sPE[s * C::LDC + t] = from_f32<E>(pe[i]);
-        sKK[s * C::LDC + t] = from_f32<E>(kkv[i]);
-      }
+      // stored transposed (row t): 4 consecutive elements a lane
+      st4(sPE + t * C::LDC + 16 * rt + 4 * lg, pe[0], pe[1], pe[2], pe[3]);
+      st4(sKK + t * C::LDC + 16 * rt + 4 * lg, kkv[0], kkv[1], kkv[2], kkv[3]);
       cs += __shfl_xor(cs, 16, 64);
       cs += __shfl_xor(cs, 32, 64);
       if (lg == 0) colp[rt][t] = cs;
@@ -1047,10 +1054,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     }
     __syncthreads();
     // ---- phase 8: dq += (dP*E) K;  dk += (dP*E)^T Q + (dKK + dKK^T) K
+    // (sPE holds (dP*E)^T, sKK dKK^T: the symmetric sum is the same)
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
-      const auto pea = M::ld(sPE + ra * C::LDC + ks * KS + EPL * lg);
-      const auto peta = M::ld_tr(sPE + ks * KS * C::LDC + 16 * rt, C::LDC);
+      const auto pea = M::ld_tr(sPE + ks * KS * C::LDC + 16 * rt, C::LDC);
+      const auto peta = M::ld(sPE + ra * C::LDC + ks * KS + EPL * lg);
       const auto ma = M::ld_sym_tr(sKK + ra * C::LDC + ks * KS + EPL * lg,
                                    sKK + ks * KS * C::LDC + 16 * rt, C::LDC);
 #pragma unroll
