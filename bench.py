@@ -246,10 +246,13 @@ def main():
              if use_cache else None)
 
     def fwd(with_cache=use_cache):
+        # with the cache the backward needs neither A nor g_cum (T and the
+        # states come from the cache), so the forward does not write them
         return gdn.chunk_gated_delta_rule_fwd(
             d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
             initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
             output_final_state=True, cp_mode=args.cp, return_states=False,
+            return_intermediates=not with_cache,
             use_qk_l2norm_in_kernel=l2, state_cache=cache if with_cache else None)
 
     def bwd(A, with_cache=use_cache):

@@ -40,7 +40,16 @@ def both(gdn, p, cp_mode, l2=False):
                                                 d["do"], dht=d["dht"], state_cache=cache, **kw)
     recompute = gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], A,
                                                d["do"], dht=d["dht"], **kw)
+    # with a cache the backward reads neither A nor anything the forward's
+    # intermediates hold: an inference-mode forward plus the cache suffices
+    cache2 = gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode)
+    gdn.chunk_gated_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                   return_intermediates=False, state_cache=cache2, **kw)
+    no_a = gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None,
+                                          d["do"], dht=d["dht"], state_cache=cache2, **kw)
     torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, no_a, with_cache):
+        assert torch.equal(x, y), f"{n}: backward with the cache depends on A"
     # both parts of the cache written: the states, then (at the next 256-byte
     # boundary) the per-chunk T
     es = d["q"].element_size()
