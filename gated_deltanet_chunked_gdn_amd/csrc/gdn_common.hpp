@@ -178,6 +178,16 @@ __device__ __forceinline__ void st4(float *p, float a, float b, float c, float d
   *reinterpret_cast<f32x4 *>(p) = f32x4{a, b, c, d};
 }
 
+// A raw buffer over [base, base + bytes): a store whose byte offset falls
+// outside the range is dropped by the hardware, so row guards need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buf_store16(const uint4 &x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // The thread index as an opaque value.  Long loops take a copy at the top of

@@ -438,6 +438,8 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
   const E *vp = reinterpret_cast<const E *>(a.v);
   const E *bp = reinterpret_cast<const E *>(a.beta);
   const E *tmat = reinterpret_cast<const E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat);
+  // pass-1 output rows are staged in the R^T buffer when they fit there
+  constexpr bool STAGE_O = WRITE_O && MODE == kMain && 64 * G::LDV <= V * G::LDC;
 
   if (c_begin >= c_end)
     return MODE == kFix ? !block_any(tiles_nonzero<E, K, V>(st), S.flag) : false;
@@ -608,7 +610,15 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
         for (int c2 = 0; c2 < NCH; ++c2)
           qs[c2] = M::mma(M::ld(sVnt + (16 * (ct0 + c2) + lr) * G::LDC + ks * KS + EPL * lg),
                           pb[ks], qs[c2]);
-      if (r < rows) {
+      if (STAGE_O) {
+        // this lane's row piece into the R^T buffer (free since phase B);
+        // the rows leave as whole rows after the next barrier
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) {
+          const f32x4 val = qs[c2] * scale;
+          st4(sRt + r * G::LDV + 16 * (ct0 + c2) + 4 * lg, val[0], val[1], val[2], val[3]);
+        }
+      } else if (r < rows) {
         char *orow = reinterpret_cast<char *>(op + (tok0 * p.Hv + h) * V) +
                      (uint32_t)r * (uint32_t)(p.Hv * V * sizeof(E));
 #pragma unroll
@@ -649,6 +659,22 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       zero_exit = !block_any(tiles_nonzero<E, K, V>(st), S.flag);
     } else {
       __syncthreads();
+    }
+    if (STAGE_O) {
+      // the staged output rows, 16 bytes a lane; rows past the chunk's end
+      // fall outside the buffer's range and are dropped (no branch, so the
+      // commit's wait for the prefetch does not wait for these stores)
+      constexpr int PR = V / G::VEC;
+      const uint32_t o_rs = (uint32_t)(p.Hv * V * sizeof(E));
+      const auto ob = raw_buffer(op + (tok0 * p.Hv + h) * V, (uint32_t)rows * o_rs);
+#pragma unroll
+      for (int m = 0; m < (64 * PR + kThreads - 1) / kThreads; ++m) {
+        const int idx = tid + kThreads * m;
+        const int rr = idx / PR, cv = idx % PR;
+        if (64 * PR % kThreads == 0 || idx < 64 * PR)
+          buf_store16(*reinterpret_cast<const uint4 *>(sRt + rr * G::LDV + cv * G::VEC), ob,
+                      (uint32_t)rr * o_rs + (uint32_t)(cv * 16));
+      }
     }
     if (c + 1 < c_end && !zero_exit) {
       fwd_commit<E, K, V, WANT_V>(pf, S, tid);
