@@ -616,8 +616,9 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   using LP = LocPref<E, K, V>;
   constexpr int PB = LP::PB;
   LP pf;
-  // global loads of V block vb of v-head hl (rows past the chunk end read 0)
-  auto load_block = [&](const LocItem &x, int hl, int vb) {
+  // global loads of V block vb of v-head hl, in two parts: the S and D
+  // blocks, then the dO and V rows (rows past the chunk end read 0)
+  auto load_sd = [&](const LocItem &x, int hl, int vb) {
     const int h = x.hq * Gq + hl;
     const int64_t cg = x.gid * p.Hv + h;
     const int v0 = vb * VB;
@@ -636,6 +637,10 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       pf.s[m] = zs;
       pf.d[m] = zd;
     }
+  };
+  auto load_ov = [&](const LocItem &x, int hl, int vb) {
+    const int h = x.hq * Gq + hl;
+    const int v0 = vb * VB;
     const char *vb_ = reinterpret_cast<const char *>(vp + (x.tok0 * p.Hv + h) * V + v0);
     const char *ob_ = reinterpret_cast<const char *>(dop + (x.tok0 * p.Hv + h) * V + v0);
 #pragma unroll
@@ -694,7 +699,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   if (blockIdx.x >= n_items) return;
   LocItem cur = item_of(blockIdx.x);
   load_head(cur, 0);
-  load_block(cur, 0, 0);
+  load_sd(cur, 0, 0);
+  load_ov(cur, 0, 0);
   load_qk(cur);
 
   for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
@@ -802,17 +808,16 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           }
         }
       }
-      // the next block (and at a v-head boundary the next T and gates) is
-      // loaded while this one is computed
+      // the next block is loaded while this one is computed: its S and D
+      // blocks here, its dO and V rows (and at a v-head boundary the next T
+      // and gates) after phase 3's MFMAs.  Issued all at once here, the
+      // eight waves' loads queue behind one another in the address unit.
       if (vb + 1 < C::NVB) {
-        load_block(cur, hl, vb + 1);
+        load_sd(cur, hl, vb + 1);
       } else if (hl + 1 < Gq) {
-        load_head(cur, hl + 1);
-        load_block(cur, hl + 1, 0);
+        load_sd(cur, hl + 1, 0);
       } else if (has_next) {  // the next item's first v-head
-        const LocItem nxt = item_of(it_next);
-        load_head(nxt, 0);
-        load_block(nxt, 0, 0);
+        load_sd(item_of(it_next), 0, 0);
       }
       __syncthreads();
       // ---- phase 2: K S, Q S; R; dq += (scale e^g dO) S^T
@@ -889,6 +894,17 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();  // R^T fully consumed before dVn^T overwrites it
+        // second part of the next block's loads
+        if (vb + 1 < C::NVB) {
+          load_ov(cur, hl, vb + 1);
+        } else if (hl + 1 < Gq) {
+          load_head(cur, hl + 1);
+          load_ov(cur, hl + 1, 0);
+        } else if (has_next) {  // the next item's first v-head
+          const LocItem nxt = item_of(it_next);
+          load_head(nxt, 0);
+          load_ov(nxt, 0, 0);
+        }
         const f32x4 dec_s = row4(sdec);
         {
           const float dec_r = sdec[ra];
