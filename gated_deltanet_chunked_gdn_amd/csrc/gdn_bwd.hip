@@ -20,7 +20,7 @@
 // only), (2) the reverse recurrence for D, context-parallel with the same
 // exact fix-up scheme mirrored (segments run from a zero leaving gradient,
 // then the true one is propagated backwards with the homogeneous recurrence
-// until it is exactly zero), (3) a chunk-parallel kernel for the local
+// until it is zero or denormal in every element), (3) a chunk-parallel kernel for the local
 // gradients, one workgroup per (chunk, q/k head) summing its v-heads' dq and
 // dk in a fixed order (no atomics).
 #include "gdn_seg.hpp"
@@ -104,9 +104,9 @@ __device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem 
 
 // Runs chunks c_end-1 down to c_begin of one (sequence, v-head), starting
 // from the leaving-state gradient in `st`.  kRMain: full reverse step.
-// kRFix: homogeneous reverse step (no dO), stops once the gradient is exactly
-// zero.  The gradient leaving every visited chunk is stored (kRMain) or
-// accumulated (kRFix) into dstates.
+// kRFix: homogeneous reverse step (no dO), stops once the gradient is zero
+// or denormal in every element.  The gradient leaving every visited chunk is
+// stored (kRMain) or accumulated (kRFix) into dstates.
 template <typename E, int K, int V, int MODE>
 __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
                                         Tiles<Geo<E, K, V>::NTS> &st, const SeqInfo &si,
@@ -141,7 +141,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
   E *dstates = reinterpret_cast<E *>(a.ws + a.wl.dstates);
 
   if (c_begin >= c_end)
-    return MODE == kRFix ? !block_any(tiles_nonzero<E, K, V>(st), S.flag) : false;
+    return MODE == kRFix ? !block_any(tiles_significant<E, K, V>(st), S.flag) : false;
   Pref<E, K, V> pf;
   {
     const int c = c_end - 1;
@@ -304,7 +304,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
     }
     tiles_to_lds_t<E, K, V>(st, sDt, tid);
     if (MODE == kRFix) {
-      zero_exit = !block_any(tiles_nonzero<E, K, V>(st), S.flag);
+      zero_exit = !block_any(tiles_significant<E, K, V>(st), S.flag);
     } else {
       __syncthreads();
     }
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < G::NTS; ++m) st[m] += e[m];
     }
-    nonzero = block_any(tiles_nonzero<E, K, V>(st), S.flag);
+    nonzero = block_any(tiles_significant<E, K, V>(st), S.flag);
   }
   if (a.dh0)
     tiles_store<E, K, V>(st, a.dh0 + ((int64_t)n * p.Hv + h) * KV,

@@ -26,13 +26,15 @@
 //          (segment 0 from the initial state), writing O and its end state H.
 //   pass 2 (segment_kernel<kFix>): segment j >= 1 propagates D = H_{j-1}
 //          through its chunks with the homogeneous recurrence (v = 0) and adds
-//          the resulting output corrections; it stops as soon as D is exactly
-//          zero (the gates decay it geometrically), recording the leftover
-//          E_j otherwise.
+//          the resulting output corrections; it stops as soon as every
+//          element of D is zero or denormal (the gates decay it
+//          geometrically; what is dropped then is below 2^-126 per element),
+//          recording the leftover E_j otherwise.
 //   pass 3 (serial_kernel): per (sequence, head), carries the remaining
 //          residual rho_{j+1} = E_j + Phi_j(rho_j) through the segments and
 //          writes the final state H_last + rho.  Every step is exact by
-//          linearity of the recurrence in the state.
+//          linearity of the recurrence in the state, up to the dropped
+//          denormal remainders.
 #include "gdn_seg.hpp"
 
 namespace gdn {
@@ -403,9 +405,10 @@ __device__ __forceinline__ void fwd_commit(const Pref<E, K, V> &pf, const Smem &
 
 // Runs chunks [c_begin, c_end) of one (sequence, v-head) starting from the
 // state in `st`.  kMain: normal recurrence, O written.  kFix: homogeneous
-// recurrence (v = 0), O incremented, stops early once the state is exactly
-// zero.  h (optional) receives (kMain) or accumulates (kFix) the state
-// entering each chunk.  Returns true when a kFix run ended on a zero state.
+// recurrence (v = 0), O incremented, stops early once the state is zero or
+// denormal in every element.  h (optional) receives (kMain) or accumulates
+// (kFix) the state entering each chunk.  Returns true when a kFix run ended
+// that way.
 template <typename E, int K, int V, int MODE, bool WRITE_O>
 __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
                                            Tiles<Geo<E, K, V>::NTS> &st, const SeqInfo &si,
@@ -442,7 +445,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
   constexpr bool STAGE_O = WRITE_O && MODE == kMain && 64 * G::LDV <= V * G::LDC;
 
   if (c_begin >= c_end)
-    return MODE == kFix ? !block_any(tiles_nonzero<E, K, V>(st), S.flag) : false;
+    return MODE == kFix ? !block_any(tiles_significant<E, K, V>(st), S.flag) : false;
   Pref<E, K, V> pf;
   {
     const int rows = min(kChunk, si.len - c_begin * kChunk);
@@ -468,6 +471,22 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
     // values here and writing the sums after phase A
     E *hs = a.h_e ? reinterpret_cast<E *>(a.h_e) + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V
                   : nullptr;
+    // fix-up pass: this lane's output elements (row 16 rt + (l & 15) of the
+    // chunk, the 4-column pieces of its wave's V half), read here and
+    // incremented in phase C
+    typename E4<E>::type o_old[NCH];
+    if (MODE == kFix && WRITE_O) {
+      const int r = 16 * rt + lr;
+      const char *orow = reinterpret_cast<const char *>(op + (tok0 * p.Hv + h) * V) +
+                         (uint32_t)r * (uint32_t)(p.Hv * V * sizeof(E));
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        o_old[c2] = typename E4<E>::type{};
+        if (r < rows)
+          o_old[c2] = *reinterpret_cast<const typename E4<E>::type *>(
+              orow + (uint32_t)((16 * (ct0 + c2) + 4 * lg) * sizeof(E)));
+      }
+    }
     TilesOld<E, K, V> hold;
     if (hs) {
       if (MODE == kFix)
@@ -627,7 +646,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
           f32x4 val = qs[c2] * scale;
           if (MODE == kFix) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) val[i] += to_f32(dst[i]);
+            for (int i = 0; i < 4; ++i) val[i] += to_f32(o_old[c2][i]);
           }
           st4(dst, val[0], val[1], val[2], val[3]);
         }
@@ -656,7 +675,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
     }
     tiles_to_lds_t<E, K, V>(st, sSt, tid);
     if (MODE == kFix) {
-      zero_exit = !block_any(tiles_nonzero<E, K, V>(st), S.flag);
+      zero_exit = !block_any(tiles_significant<E, K, V>(st), S.flag);
     } else {
       __syncthreads();
     }
@@ -790,7 +809,7 @@ __global__ __launch_bounds__(kThreads) void serial_kernel(FwdArgs a) {
 #pragma unroll
       for (int m = 0; m < G::NTS; ++m) st[m] += e[m];
     }
-    nonzero = block_any(tiles_nonzero<E, K, V>(st), S.flag);
+    nonzero = block_any(tiles_significant<E, K, V>(st), S.flag);
   }
   if (a.ht)
     tiles_store<E, K, V>(st, a.ht + ((int64_t)n * p.Hv + h) * KV,

@@ -415,13 +415,18 @@ __device__ __forceinline__ void tiles_to_lds_t(const Tiles<Geo<E, K, V>::NTS> &s
   }
 }
 
+// True when some element of the (correction) state has magnitude at least
+// 2^-126, the smallest normal fp32.  The fix-up passes stop once it fails:
+// what they drop is a state whose every element is zero or denormal, so its
+// further contributions are of order 2^-126 (the decay drives a correction
+// through the denormal range in about one more chunk).
 template <typename E, int K, int V>
-__device__ __forceinline__ bool tiles_nonzero(const Tiles<Geo<E, K, V>::NTS> &s) {
+__device__ __forceinline__ bool tiles_significant(const Tiles<Geo<E, K, V>::NTS> &s) {
   bool nz = false;
 #pragma unroll
   for (int m = 0; m < Geo<E, K, V>::NTS; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nz |= (s[m][i] != 0.f);
+    for (int i = 0; i < 4; ++i) nz |= (__builtin_fabsf(s[m][i]) >= 0x1p-126f);
   return nz;
 }
 
