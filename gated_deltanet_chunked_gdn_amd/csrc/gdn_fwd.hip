@@ -75,12 +75,16 @@ struct PrepCfg {
   static constexpr int bytesK = 64 * LDK * (int)sizeof(E);
   // per wave, 16x16 fp32 blocks with row stride 17 (the MFMA operand reads
   // of 16 rows x 4 columns then hit distinct banks): the 6 off-diagonal A
-  // blocks, the 10 lower blocks of T, one product; plus the 4 diagonal A
-  // blocks transposed with row stride 20 (float4 reads)
+  // blocks, the 10 lower blocks of T (the 4 diagonal ones first), one
+  // product.  The 4 diagonal A blocks, transposed with row stride 20 (float4
+  // reads), share the space of T's off-diagonal blocks: they are dead once
+  // the diagonal blocks are inverted, before any off-diagonal block is
+  // written.  (19 KB a wave: four 2-wave workgroups fit a compute unit.)
   static constexpr int BS = 16 * 17;
-  static constexpr int fA = 0, fT = 6 * BS, fM = 16 * BS, fAd = 17 * BS;
+  static constexpr int fA = 0, fT = 6 * BS, fM = 16 * BS, fAd = fT + 4 * BS;
+  static_assert(4 * 16 * 20 <= 6 * BS, "diagonal A blocks fit the off-diagonal T space");
   // gamma log2(e) and beta of the chunk rows
-  static constexpr int fG = fAd + 4 * 16 * 20, fB = fG + 64;
+  static constexpr int fG = fM + BS, fB = fG + 64;
   static constexpr int floatsW = fB + 64;
   static constexpr int bytesW = floatsW * 4;
 };
@@ -189,8 +193,9 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
   float *W = reinterpret_cast<float *>(smem) + w * C::floatsW;
   float *sA = W + C::fA, *sT = W + C::fT, *sAd = W + C::fAd, *sM = W + C::fM;
   constexpr int LD = 17, BS = C::BS;
-  // lower block (i >= j) of T, off-diagonal block (i > j) of A
-#define TB(i, j) (sT + (((i) * ((i) + 1)) / 2 + (j)) * BS)
+  // lower block (i >= j) of T (diagonal blocks first), off-diagonal block
+  // (i > j) of A
+#define TB(i, j) (sT + ((i) == (j) ? (i) : 4 + ((i) * ((i) - 1)) / 2 + (j)) * BS)
 #define AB(i, j) (sA + (((i) * ((i) - 1)) / 2 + (j)) * BS)
   E *tmat = reinterpret_cast<E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat);
   for (int hl = w; hl < G; hl += nw) {
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
           if (r0 + 3 > j) x[r0 + 3] += a4.w * x[j];
         }
       }
-      float *tb = sT + ((b * (b + 1)) / 2 + b) * BS;
+      float *tb = TB(b, b);
 #pragma unroll
       for (int r = 0; r < 16; ++r) tb[r * LD + c] = x[r];
     }
@@ -297,7 +302,7 @@ __global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
       const int rb = r >> 4, cb = c0 >> 4;
       float x[4] = {0.f, 0.f, 0.f, 0.f};
       if (cb <= rb) {
-        const float *src = sT + (((rb * (rb + 1)) / 2) + cb) * BS + (r & 15) * LD + (c0 & 15);
+        const float *src = TB(rb, cb) + (r & 15) * LD + (c0 & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = src[e];
       }
