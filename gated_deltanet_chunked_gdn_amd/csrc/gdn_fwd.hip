@@ -114,203 +114,267 @@ __device__ __forceinline__ void put16(float *dst, int ld, f32x4 c, float sgn) {
   for (int i = 0; i < 4; ++i) dst[(4 * lg + i) * ld + lr] = sgn * c[i];
 }
 
+// Two waves a workgroup, each taking every other v-head of the item's q/k
+// head (the second wave idles when there is one v-head per q/k head).
+constexpr int kPrepThreads = 128;
+
 template <typename E, int K>
-__global__ __launch_bounds__(256) void prep_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2))) void prep_kernel(
+    FwdArgs a) {
   using C = PrepCfg<E, K>;
   using M = Mma<E>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   E *sK = reinterpret_cast<E *>(smem);
   const Problem &p = a.p;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int nw = blockDim.x >> 6;
+  constexpr int nw = kPrepThreads / 64;
   const int G = p.Hv / p.Hq;
-  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int hq = (int)(wid % p.Hq);
-  const int64_t gid = wid / p.Hq;
-  const ChunkLoc cl =
-      locate_chunk(p, reinterpret_cast<const int32_t *>(a.ws + a.wl.chunk_prefix), gid);
-  const int64_t tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
-  const int rows = min(kChunk, cl.si.len - cl.c * kChunk);
-
-  // raw gate and beta of this wave's next v-head, loaded one v-head ahead
-  // (the first together with the k tile)
+  const int lr = lane & 15, lg = lane >> 4;
+  // Work items are (chunk, q/k head) pairs; a workgroup takes items
+  // blockIdx.x, + gridDim.x, ... and loads the next item's k tile, gates and
+  // beta while it computes the current one.
+  const int64_t n_items = a.plan.total_chunks * p.Hq;
+  struct Item {
+    int hq, rows;
+    int64_t gid, tok0;
+  };
+  auto item_of = [&](int64_t it) {
+    Item x;
+    x.hq = (int)(it % p.Hq);
+    x.gid = it / p.Hq;
+    const ChunkLoc cl =
+        locate_chunk(p, reinterpret_cast<const int32_t *>(a.ws + a.wl.chunk_prefix), x.gid);
+    x.tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
+    x.rows = min(kChunk, cl.si.len - cl.c * kChunk);
+    return x;
+  };
+  // raw gate and beta of this wave's next v-head (one v-head ahead)
   float gv_n = 0.f, bv_n = 0.f;
-  auto load_gb = [&](int hl) {
+  auto load_gb = [&](const Item &x, int hl) {
     gv_n = 0.f;
     bv_n = 0.f;
-    if (hl < G && lane < rows) {
-      const int64_t gi = (tok0 + lane) * p.Hv + hq * G + hl;
+    if (hl < G && lane < x.rows) {
+      const int64_t gi = (x.tok0 + lane) * p.Hv + x.hq * G + hl;
       gv_n = a.g[gi];
       bv_n = to_f32(reinterpret_cast<const E *>(a.beta)[gi]);
     }
   };
-  load_gb(w);
   const E *kp = reinterpret_cast<const E *>(a.k);
   constexpr int VEC = 16 / (int)sizeof(E);
   constexpr int PR = K / VEC;
-  {
-    // every load in flight before the first LDS store (1 or 2 waves)
-    constexpr int NP = PR;  // pieces per thread for one wave
-    uint4 val[NP];
+  constexpr int NP = (64 * PR + kPrepThreads - 1) / kPrepThreads;  // 16-byte pieces a thread
+  uint4 kv[NP];
+  auto load_k = [&](const Item &x) {
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-      const int idx = tid + (int)blockDim.x * m;
+      const int idx = tid + kPrepThreads * m;
       const int r = idx / PR, cv = idx % PR;
-      val[m] = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < 64 * PR && r < rows)
-        val[m] = *reinterpret_cast<const uint4 *>(kp + ((tok0 + r) * p.Hq + hq) * K + cv * VEC);
+      kv[m] = make_uint4(0u, 0u, 0u, 0u);
+      if (idx < 64 * PR && r < x.rows)
+        kv[m] = *reinterpret_cast<const uint4 *>(kp + ((x.tok0 + r) * p.Hq + x.hq) * K + cv * VEC);
     }
-#pragma unroll
-    for (int m = 0; m < NP; ++m) {
-      const int idx = tid + (int)blockDim.x * m;
-      const int r = idx / PR, cv = idx % PR;
-      if (idx < 64 * PR) *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = val[m];
-    }
-  }
-  __syncthreads();
-  const int lr = lane & 15, lg = lane >> 4;
-  f32x4 kk[10];
-  {
-    int t = 0;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int ct = 0; ct <= rt; ++ct) kk[t++] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < K / M::KS; ++ks) {
-      typename M::frag x[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        x[rt] = M::ld(sK + (16 * rt + lr) * C::LDK + ks * M::KS + M::EPL * lg);
-      t = 0;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct <= rt; ++ct, ++t) kk[t] = M::mma(x[rt], x[ct], kk[t]);
-    }
-  }
-  __syncthreads();  // the per-wave buffers alias sK
+  };
+  if (blockIdx.x >= n_items) return;
+  Item cur = item_of(blockIdx.x);
+  load_gb(cur, w);
+  load_k(cur);
+  E *tmat = reinterpret_cast<E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat);
+  constexpr int LD = 17, BS = C::BS;
   float *W = reinterpret_cast<float *>(smem) + w * C::floatsW;
   float *sA = W + C::fA, *sT = W + C::fT, *sAd = W + C::fAd, *sM = W + C::fM;
-  constexpr int LD = 17, BS = C::BS;
   // lower block (i >= j) of T (diagonal blocks first), off-diagonal block
   // (i > j) of A
 #define TB(i, j) (sT + ((i) == (j) ? (i) : 4 + ((i) * ((i) - 1)) / 2 + (j)) * BS)
 #define AB(i, j) (sA + (((i) * ((i) - 1)) / 2 + (j)) * BS)
-  E *tmat = reinterpret_cast<E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat);
-  for (int hl = w; hl < G; hl += nw) {
-    const int h = hq * G + hl;
-    const int64_t gi = (tok0 + lane) * p.Hv + h;
-    const float gv = gv_n, bv = bv_n;
-    load_gb(hl + nw);
-    const float gam = wave_incl_scan(gv);
-    float *sG = W + C::fG, *sB = W + C::fB;
-    sG[lane] = gam * kLog2e;
-    sB[lane] = bv;
-    wave_sync();
-    // A = strict_lower(beta_r exp(gamma_r - gamma_j) KK): off-diagonal blocks
-    // row-major, diagonal blocks transposed
+
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int64_t it_next = it + gridDim.x;
+    const bool has_next = it_next < n_items;
+    const int hq = cur.hq, rows = cur.rows;
+    const int64_t gid = cur.gid, tok0 = cur.tok0;
+    // the k tile into LDS (the per-wave buffers that alias it are free)
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int idx = tid + kPrepThreads * m;
+      const int r = idx / PR, cv = idx % PR;
+      if (idx < 64 * PR) *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = kv[m];
+    }
+    __syncthreads();
+    f32x4 kk[10];
     {
       int t = 0;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int ct = 0; ct <= rt; ++ct, ++t) {
-          const int j = 16 * ct + lr;
-          const float gj = sG[j];
-          const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(sG + 16 * rt + 4 * lg);
-          const f32x4 br4 = *reinterpret_cast<const f32x4 *>(sB + 16 * rt + 4 * lg);
+        for (int ct = 0; ct <= rt; ++ct) kk[t++] = zero4();
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * rt + 4 * lg + i;
-            const float val =
-                (j < r) ? br4[i] * __builtin_amdgcn_exp2f(gr4[i] - gj) * kk[t][i] : 0.f;
-            if (ct == rt)
-              sAd[(rt * 16 + lr) * 20 + 4 * lg + i] = val;
-            else
-              AB(rt, ct)[(4 * lg + i) * LD + lr] = val;
+      for (int ks = 0; ks < K / M::KS; ++ks) {
+        typename M::frag x[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          x[rt] = M::ld(sK + (16 * rt + lr) * C::LDK + ks * M::KS + M::EPL * lg);
+        t = 0;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int ct = 0; ct <= rt; ++ct, ++t) kk[t] = M::mma(x[rt], x[ct], kk[t]);
+      }
+    }
+    __syncthreads();  // the per-wave buffers alias sK
+    Item nxt = cur;
+    if (has_next) {
+      nxt = item_of(it_next);
+      load_k(nxt);
+    }
+    for (int hl = w; hl < G; hl += nw) {
+      const int h = hq * G + hl;
+      const int64_t gi = (tok0 + lane) * p.Hv + h;
+      const float gv = gv_n, bv = bv_n;
+      if (hl + nw < G)
+        load_gb(cur, hl + nw);
+      else if (has_next)
+        load_gb(nxt, w);
+      const float gam = wave_incl_scan(gv);
+      float *sG = W + C::fG, *sB = W + C::fB;
+      sG[lane] = gam * kLog2e;
+      sB[lane] = bv;
+      wave_sync();
+      // A = strict_lower(beta_r exp(gamma_r - gamma_j) KK): off-diagonal
+      // blocks row-major, diagonal blocks transposed
+      {
+        int t = 0;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int ct = 0; ct <= rt; ++ct, ++t) {
+            const int j = 16 * ct + lr;
+            const float gj = sG[j];
+            const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(sG + 16 * rt + 4 * lg);
+            const f32x4 br4 = *reinterpret_cast<const f32x4 *>(sB + 16 * rt + 4 * lg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * rt + 4 * lg + i;
+              const float val =
+                  (j < r) ? br4[i] * __builtin_amdgcn_exp2f(gr4[i] - gj) * kk[t][i] : 0.f;
+              if (ct == rt)
+                sAd[(rt * 16 + lr) * 20 + 4 * lg + i] = val;
+              else
+                AB(rt, ct)[(4 * lg + i) * LD + lr] = val;
+            }
+          }
+      }
+      wave_sync();
+      // diagonal blocks: lane = (block b, column c)
+      {
+        const int b = lane >> 4, c = lane & 15;
+        const float *at = sAd + b * 16 * 20;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          x[j] = (j == c ? 1.f : 0.f) - x[j];
+#pragma unroll
+          for (int r0 = (j + 1) & ~3; r0 < 16; r0 += 4) {
+            const float4 a4 = *reinterpret_cast<const float4 *>(at + j * 20 + r0);
+            if (r0 + 0 > j) x[r0 + 0] += a4.x * x[j];
+            if (r0 + 1 > j) x[r0 + 1] += a4.y * x[j];
+            if (r0 + 2 > j) x[r0 + 2] += a4.z * x[j];
+            if (r0 + 3 > j) x[r0 + 3] += a4.w * x[j];
           }
         }
-    }
-    wave_sync();
-    // diagonal blocks: lane = (block b, column c)
-    {
-      const int b = lane >> 4, c = lane & 15;
-      const float *at = sAd + b * 16 * 20;
-      float x[16];
+        float *tb = TB(b, b);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = 0.f;
+        for (int r = 0; r < 16; ++r) tb[r * LD + c] = x[r];
+      }
+      wave_sync();
+      // level 1: T_{b+1,b} = -T_{b+1,b+1} A_{b+1,b} T_bb
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        x[j] = (j == c ? 1.f : 0.f) - x[j];
+      for (int b = 0; b < 3; ++b) {
+        f32x4 m = mm16(zero4(), AB(b + 1, b), TB(b, b), LD);
+        put16(sM, LD, m, 1.f);
+        wave_sync();
+        f32x4 t1 = mm16(zero4(), TB(b + 1, b + 1), sM, LD);
+        wave_sync();
+        put16(TB(b + 1, b), LD, t1, -1.f);
+      }
+      wave_sync();
+      // level 2: T_{b+2,b} = -T_{b+2,b+2} (A_{b+2,b} T_bb + A_{b+2,b+1} T_{b+1,b})
 #pragma unroll
-        for (int r0 = (j + 1) & ~3; r0 < 16; r0 += 4) {
-          const float4 a4 = *reinterpret_cast<const float4 *>(at + j * 20 + r0);
-          if (r0 + 0 > j) x[r0 + 0] += a4.x * x[j];
-          if (r0 + 1 > j) x[r0 + 1] += a4.y * x[j];
-          if (r0 + 2 > j) x[r0 + 2] += a4.z * x[j];
-          if (r0 + 3 > j) x[r0 + 3] += a4.w * x[j];
+      for (int b = 0; b < 2; ++b) {
+        f32x4 m = mm16(zero4(), AB(b + 2, b), TB(b, b), LD);
+        m = mm16(m, AB(b + 2, b + 1), TB(b + 1, b), LD);
+        put16(sM, LD, m, 1.f);
+        wave_sync();
+        f32x4 t2 = mm16(zero4(), TB(b + 2, b + 2), sM, LD);
+        wave_sync();
+        put16(TB(b + 2, b), LD, t2, -1.f);
+      }
+      wave_sync();
+      // level 3: T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
+      {
+        f32x4 m = mm16(zero4(), AB(3, 0), TB(0, 0), LD);
+        m = mm16(m, AB(3, 1), TB(1, 0), LD);
+        m = mm16(m, AB(3, 2), TB(2, 0), LD);
+        put16(sM, LD, m, 1.f);
+        wave_sync();
+        f32x4 t3 = mm16(zero4(), TB(3, 3), sM, LD);
+        put16(TB(3, 0), LD, t3, -1.f);
+      }
+      wave_sync();
+      // T out (element type, chunk-contiguous rows), 16 bytes a lane, in two
+      // halves: each half's values are read from the blocks before its first
+      // store.  Pieces of upper blocks read some other block and store 0.
+      {
+        E *tm = tmat + (gid * p.Hv + h) * 64 * 64;
+        constexpr int TPR = 64 / VEC;  // pieces per row
+        constexpr int TNP = TPR / 2;   // pieces per lane and half
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint4 tv[TNP];
+#pragma unroll
+          for (int q = 0; q < TNP; ++q) {
+            const int idx = lane + 64 * (q + TNP * half);
+            const int r = idx / TPR, c0 = (idx % TPR) * VEC;
+            const int rb = r >> 4, cb = c0 >> 4;
+            const float *src = TB(rb, cb) + (r & 15) * LD + (c0 & 15);
+            E *o = reinterpret_cast<E *>(&tv[q]);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              const float v = src[e];
+              o[e] = from_f32<E>(cb <= rb ? v : 0.f);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < TNP; ++q) {
+            const int idx = lane + 64 * (q + TNP * half);
+            const int r = idx / TPR, c0 = (idx % TPR) * VEC;
+            *reinterpret_cast<uint4 *>(tm + r * 64 + c0) = tv[q];
+          }
         }
       }
-      float *tb = TB(b, b);
+      // fp32 A (rows at their tokens) and the gate cumsum, when asked for
+      if (a.A) {
+        float *arow = a.A + (tok0 * p.Hv + h) * 64;
+#pragma unroll 1
+        for (int q = 0; q < 16; ++q) {
+          const int idx = lane + 64 * q;
+          const int r = idx >> 4, c0 = (idx & 15) * 4;
+          const int rb = r >> 4, cb = c0 >> 4;
+          float x[4] = {0.f, 0.f, 0.f, 0.f};
+          if (cb <= rb) {
+            const float *src = TB(rb, cb) + (r & 15) * LD + (c0 & 15);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tb[r * LD + c] = x[r];
-    }
-    wave_sync();
-    // level 1: T_{b+1,b} = -T_{b+1,b+1} A_{b+1,b} T_bb
-#pragma unroll
-    for (int b = 0; b < 3; ++b) {
-      f32x4 m = mm16(zero4(), AB(b + 1, b), TB(b, b), LD);
-      put16(sM, LD, m, 1.f);
-      wave_sync();
-      f32x4 t1 = mm16(zero4(), TB(b + 1, b + 1), sM, LD);
-      wave_sync();
-      put16(TB(b + 1, b), LD, t1, -1.f);
-    }
-    wave_sync();
-    // level 2: T_{b+2,b} = -T_{b+2,b+2} (A_{b+2,b} T_bb + A_{b+2,b+1} T_{b+1,b})
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x4 m = mm16(zero4(), AB(b + 2, b), TB(b, b), LD);
-      m = mm16(m, AB(b + 2, b + 1), TB(b + 1, b), LD);
-      put16(sM, LD, m, 1.f);
-      wave_sync();
-      f32x4 t2 = mm16(zero4(), TB(b + 2, b + 2), sM, LD);
-      wave_sync();
-      put16(TB(b + 2, b), LD, t2, -1.f);
-    }
-    wave_sync();
-    // level 3: T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
-    {
-      f32x4 m = mm16(zero4(), AB(3, 0), TB(0, 0), LD);
-      m = mm16(m, AB(3, 1), TB(1, 0), LD);
-      m = mm16(m, AB(3, 2), TB(2, 0), LD);
-      put16(sM, LD, m, 1.f);
-      wave_sync();
-      f32x4 t3 = mm16(zero4(), TB(3, 3), sM, LD);
-      put16(TB(3, 0), LD, t3, -1.f);
-    }
-    wave_sync();
-    // T out, 4 consecutive columns per lane: element type (internal,
-    // chunk-contiguous rows) and fp32 A (rows at their tokens)
-    E *tm = tmat + (gid * p.Hv + h) * 64 * 64;
-    float *arow = a.A ? a.A + (tok0 * p.Hv + h) * 64 : nullptr;
-#pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int idx = lane + 64 * it;
-      const int r = idx >> 4, c0 = (idx & 15) * 4;
-      const int rb = r >> 4, cb = c0 >> 4;
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
-      if (cb <= rb) {
-        const float *src = TB(rb, cb) + (r & 15) * LD + (c0 & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = src[e];
+            for (int e = 0; e < 4; ++e) x[e] = src[e];
+          }
+          if (r < rows) st4(arow + (uint32_t)(r * p.Hv * 64 + c0), x[0], x[1], x[2], x[3]);
+        }
       }
-      st4(tm + r * 64 + c0, x[0], x[1], x[2], x[3]);
-      if (arow && r < rows) st4(arow + (uint32_t)(r * p.Hv * 64 + c0), x[0], x[1], x[2], x[3]);
+      if (a.g_cum && lane < rows) a.g_cum[gi] = gam;
+      wave_sync();
     }
-    if (a.g_cum && lane < rows) a.g_cum[gi] = gam;
-    wave_sync();
+    __syncthreads();  // the per-wave buffers are read out before the next k tile lands
+    cur = nxt;
   }
 #undef TB
 #undef AB
@@ -832,11 +896,14 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
     return;
   }
   using C = PrepCfg<E, K>;
-  const int G = p.Hv / p.Hq;
-  const int nw = G < 2 ? G : 2;
+  constexpr int nw = kPrepThreads / 64;
   const size_t lds = (size_t)(C::bytesK > nw * C::bytesW ? C::bytesK : nw * C::bytesW);
+  // persistent: as many workgroups as the LDS lets the compute units hold
+  const int64_t items = pl.total_chunks * p.Hq;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (int64_t)lds));
+  const int64_t grid = std::min<int64_t>(items, per_cu * (pl.cus > 0 ? pl.cus : 256));
   KernelTimer kt("prep", st);
-  prep_kernel<E, K><<<dim3((unsigned)(pl.total_chunks * p.Hq)), 64 * nw, lds, st>>>(a);
+  prep_kernel<E, K><<<dim3((unsigned)grid), kPrepThreads, lds, st>>>(a);
 }
 
 // Stage bits of launch_fwd_t: the plan prefix sums and prep (T from k or
