@@ -148,15 +148,17 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
     x.rows = min(kChunk, cl.si.len - cl.c * kChunk);
     return x;
   };
-  // raw gate and beta of this wave's next v-head (one v-head ahead)
-  float gv_n = 0.f, bv_n = 0.f;
+  // raw gate and beta of this wave's next v-head (one v-head ahead; beta
+  // stays in the element type until used, so nothing waits for the load)
+  float gv_n = 0.f;
+  E bv_n = from_f32<E>(0.f);
   auto load_gb = [&](const Item &x, int hl) {
     gv_n = 0.f;
-    bv_n = 0.f;
+    bv_n = from_f32<E>(0.f);
     if (hl < G && lane < x.rows) {
       const int64_t gi = (x.tok0 + lane) * p.Hv + x.hq * G + hl;
       gv_n = a.g[gi];
-      bv_n = to_f32(reinterpret_cast<const E *>(a.beta)[gi]);
+      bv_n = reinterpret_cast<const E *>(a.beta)[gi];
     }
   };
   const E *kp = reinterpret_cast<const E *>(a.k);
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
     for (int hl = w; hl < G; hl += nw) {
       const int h = hq * G + hl;
       const int64_t gi = (tok0 + lane) * p.Hv + h;
-      const float gv = gv_n, bv = bv_n;
+      const float gv = gv_n, bv = to_f32(bv_n);
       if (hl + nw < G)
         load_gb(cur, hl + nw);
       else if (has_next)
