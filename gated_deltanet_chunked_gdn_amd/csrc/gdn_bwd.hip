@@ -430,11 +430,13 @@ __global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
 template <typename E, int K, int V>
 struct LocCfg {
   using G = Geo<E, K, V>;
-  // row pitches: 16 bytes of padding (the segment kernels pad 32 bytes, which
-  // this kernel's LDS footprint has no room for)
+  // row pitches: q, k, T, P^T (and the 64-wide buffers that share LDC) pad
+  // 32 bytes, which keeps their 16-byte fragment reads free of bank
+  // conflicts; the V-block buffers pad 16 bytes (the LDS footprint has no
+  // room for more)
   static constexpr int PAD = 16 / (int)sizeof(E);
-  static constexpr int LDK = K + PAD;
-  static constexpr int LDC = 64 + PAD;
+  static constexpr int LDK = K + 32 / (int)sizeof(E);
+  static constexpr int LDC = 64 + 32 / (int)sizeof(E);
   static constexpr int VB = (sizeof(E) == 4) ? 32 : (V < 64 ? V : 64);
   static constexpr int NVB = V / VB;
   static constexpr int LDB = VB + PAD;
