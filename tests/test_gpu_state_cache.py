@@ -9,11 +9,12 @@ pass of segments past the first (forced short segments), the serial residual
 pass (gates that do not decay), packed sequences with empty ones, an initial
 state, fp32 and the in-library q/k normalisation.
 """
+import numpy as np
 import pytest
 import torch
 
 import synth
-from tests.gpu_util import TOL, announce, oracle_bwd, rel, to_dev
+from tests.gpu_util import TOL, announce, oracle_bwd, oracle_fwd, rel, to_dev, token_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -105,3 +106,45 @@ def test_cache_matches_recompute_and_oracle(gdn, case):
         errs = {n: rel(x, r) for n, x, r in zip(NAMES, got, ref)}
         bad = {n: e for n, e in errs.items() if not e <= TOL[dtype]}
         assert not bad, f"{label}: {bad} (all: {errs})"
+
+
+def test_full_hv64_t8192_cached_step(gdn):
+    """The benchmark's own step at its full size and in its launch
+    configuration: the training forward fills the cache (no A, no g_cum), the
+    backward takes it with A = None.  o, the final state and every gradient
+    are checked against the oracle on whole q/k groups: v-heads 0, 1 (q/k
+    head 0), 40, 41 (q/k head 20) and 62, 63 (q/k head 31)."""
+    w = synth.WORKLOADS["hv64_t8192"]
+    p = synth.make(w, with_grads=True)
+    announce("full hv64_t8192 cached fwd+bwd")
+    d = to_dev(p)
+    kw = dict(scale=d["scale"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"])
+    cache = gdn.state_cache_empty(d["q"], d["v"])
+    _, A, o, _, ht = gdn.chunk_gated_delta_rule_fwd(
+        d["q"], d["k"], d["v"], d["g"], d["beta"], output_final_state=True,
+        return_intermediates=False, return_states=False, state_cache=cache, **kw)
+    assert A is None
+    got = gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None,
+                                         d["do"], dht=d["dht"], state_cache=cache, **kw)
+    torch.cuda.synchronize()
+    heads = [0, 1, 40, 41, 62, 63]
+    mask = np.zeros((w.B, w.Hv), dtype=bool)
+    mask[:, heads] = True
+    tm = token_mask(p, mask)
+    ro, rht = oracle_fwd(p, unit_mask=mask)
+    errs = {"o": rel(o.double().cpu().numpy()[tm], ro[tm]),
+            "ht": rel(ht.double().cpu().numpy()[mask], rht[mask])}
+    ref = oracle_bwd(p, unit_mask=mask)
+    grp = w.Hv // w.Hq
+    qk_heads = sorted({h // grp for h in heads})
+    for n, x, r in zip(NAMES, got, ref):
+        x = x.double().cpu().numpy()
+        assert np.isfinite(x).all(), n
+        if n in ("dq", "dk"):
+            errs[n] = rel(x[:, :, qk_heads], r[:, :, qk_heads])
+        elif n == "dh0":
+            errs[n] = rel(x[mask], r[mask])
+        else:
+            errs[n] = rel(x[tm], r[tm])
+    bad = {n: e for n, e in errs.items() if not e <= TOL[w.dtype]}
+    assert not bad, f"{bad} (all {errs})"
