@@ -430,33 +430,33 @@ __global__ __launch_bounds__(kThreads) void rev_serial_kernel(BwdArgs a) {
 template <typename E, int K, int V>
 struct LocCfg {
   using G = Geo<E, K, V>;
-  // row pitches: q, k, T, P^T (and the 64-wide buffers that share LDC) pad
-  // 32 bytes, which keeps their 16-byte fragment reads free of bank
-  // conflicts; the V-block buffers pad 16 bytes (the LDS footprint has no
-  // room for more)
+  // row pitches: bf16 rows pad 32 bytes, which keeps their 16-byte fragment
+  // reads free of bank conflicts; fp32 V-block rows and S/D rows pad 16
+  // bytes (the fp32 footprint has no room for more)
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = K + 32 / (int)sizeof(E);
   static constexpr int LDC = 64 + 32 / (int)sizeof(E);
   static constexpr int VB = (sizeof(E) == 4) ? 32 : (V < 64 ? V : 64);
   static constexpr int NVB = V / VB;
-  static constexpr int LDB = VB + PAD;
+  static constexpr int LDB = VB + (sizeof(E) == 2 ? 16 : PAD);
   static constexpr int NCHB = VB / 32;  // V-block column tiles per half
   static constexpr int NCHK = K / 32;   // key column tiles per half
-  static constexpr int LDSK = K + PAD;  // rows of the transposed S and D blocks
+  static constexpr int LDSK = K + (sizeof(E) == 2 ? 16 : PAD);  // rows of the transposed S and D blocks
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + 64 * LDK;
   static constexpr int oT = oK + 64 * LDK;
   static constexpr int oPt = oT + 64 * LDC;
   // V-block buffers (dead after the V-block loop)
-  static constexpr int oS = oPt + 64 * LDC;     // S^T block [VB][LDSK]
-  static constexpr int oD = oS + VB * LDSK;     // D^T block [VB][LDSK]; later dR [64][LDB]
-  static constexpr int oDO = oD + (VB * LDSK > 64 * LDB ? VB * LDSK : 64 * LDB);  // dO block [64][LDB]
-  static constexpr int oDOq = oDO + 64 * LDB;      // dO rows * scale e^gamma
-  static constexpr int oRt = oDOq + 64 * LDB;      // R^T [VB][LDC]; later dVn^T
-  static constexpr int oVn = oRt + VB * LDC;    // Vn [64][LDB]
-  static constexpr int oVnd = oVn + 64 * LDB;      // Vn rows * e^{gamma_L - gamma}
-  static constexpr int oDRs = oVnd + 64 * LDB;     // dR rows * (-beta e^gamma)
-  static constexpr int oV = oDRs + 64 * LDB;       // V block [64][LDB]
+  // (every buffer of its own: no phase waits for another's readers before
+  // it writes; row-scaled operands are scaled in registers)
+  static constexpr int oS = oPt + 64 * LDC;      // S^T block [VB][LDSK]
+  static constexpr int oD = oS + VB * LDSK;      // D^T block [VB][LDSK]
+  static constexpr int oDO = oD + VB * LDSK;     // dO block [64][LDB]
+  static constexpr int oRt = oDO + 64 * LDB;     // R^T [VB][LDC]
+  static constexpr int oDVnt = oRt + VB * LDC;   // dVn^T [VB][LDC]
+  static constexpr int oVn = oDVnt + VB * LDC;   // Vn [64][LDB]
+  static constexpr int oDR = oVn + 64 * LDB;     // dR [64][LDB]
+  static constexpr int oV = oDR + 64 * LDB;      // V block [64][LDB]; later dv
   static constexpr int nE = oV + 64 * LDB;
   // after the V-block loop: dP * E and dKK [64][LDC] reuse the block buffers
   static constexpr int oPE = oS;
@@ -525,14 +525,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   E *sPt = sm + C::oPt;
   E *sS = sm + C::oS;
   E *sD = sm + C::oD;
-  E *sDR = sm + C::oD;  // dR reuses the D block after its last use
+  E *sDR = sm + C::oDR;
   E *sDO = sm + C::oDO;
   E *sRt = sm + C::oRt;
-  E *sDVnt = sm + C::oRt;
+  E *sDVnt = sm + C::oDVnt;
   E *sVn = sm + C::oVn;
-  E *sDOq = sm + C::oDOq;
-  E *sVnd = sm + C::oVnd;
-  E *sDRs = sm + C::oDRs;
   E *sPE = sm + C::oPE;
   E *sKK = sm + C::oKK;
   E *sV = sm + C::oV;
@@ -803,9 +800,6 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           if (idx < 64 * PB) {
             const int r = idx / PB, cv = idx % PB;
             *reinterpret_cast<uint4 *>(sDO + r * LDB + cv * VEC) = pf.o[m];
-            // dq += (scale e^g dO) S^T takes dO with its rows scaled
-            *reinterpret_cast<uint4 *>(sDOq + r * LDB + cv * VEC) =
-                scale_piece<E>(pf.o[m], scale * seg[r]);
             *reinterpret_cast<uint4 *>(sV + r * LDB + cv * VEC) = pf.v[m];
           }
         }
@@ -857,9 +851,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         st4(sRt + vc * C::LDC + 16 * rt + 4 * lg, rr[0], rr[1], rr[2], rr[3]);
       }
       }
+      // dq += (scale e^g dO) S^T: the dO rows scaled in registers
+      const float dq_s = scale * seg[ra];
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
-        const auto da_ = M::ld(sDOq + ra * LDB + ks * KS + EPL * lg);
+        const auto da_ = M::scaled(M::ld(sDO + ra * LDB + ks * KS + EPL * lg), dq_s);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
           dq[m] = M::mma(da_, M::ld_tr(sS + ks * KS * C::LDSK + 16 * (ch * NCHK + m), C::LDSK),
@@ -895,7 +891,6 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
                 kd[m]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();  // R^T fully consumed before dVn^T overwrites it
         // second part of the next block's loads
         if (vb + 1 < C::NVB) {
           load_ov(cur, hl, vb + 1);
@@ -909,15 +904,10 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         }
         const f32x4 dec_s = row4(sdec);
         {
-          const float dec_r = sdec[ra];
 #pragma unroll
-          for (int m = 0; m < NCHB; ++m) {
-            E *o = sVn + ra * LDB + 16 * (ch * NCHB + m) + 4 * lg;
-            st4(o, vn[m][0], vn[m][1], vn[m][2], vn[m][3]);
-            // dk += (e^{gL-g} Vn) D^T takes Vn with its rows scaled
-            st4(sVnd + (o - sVn), dec_r * vn[m][0], dec_r * vn[m][1], dec_r * vn[m][2],
-                dec_r * vn[m][3]);
-          }
+          for (int m = 0; m < NCHB; ++m)
+            st4(sVn + ra * LDB + 16 * (ch * NCHB + m) + 4 * lg, vn[m][0], vn[m][1], vn[m][2],
+                vn[m][3]);
           // c_r = e^{gL-g_r} <Vn_r, (K D)_r>: Vn read back at the K D tiles'
           // accumulator positions (this wave's own tiles)
 #pragma unroll
@@ -951,9 +941,11 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       }
       __syncthreads();
       // ---- phase 4b: dk += (dec Vn) D^T;  phase 5: dR = T^T dVn, dv, dbeta/de rows
+      // dk += (e^{gL-g} Vn) D^T: the Vn rows scaled in registers
+      const float dk_s = sdec[ra];
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
-        const auto vna = M::ld(sVnd + ra * LDB + ks * KS + EPL * lg);
+        const auto vna = M::scaled(M::ld(sVn + ra * LDB + ks * KS + EPL * lg), dk_s);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
           dk[m] = M::mma(vna, M::ld_tr(sD + ks * KS * C::LDSK + 16 * (ch * NCHK + m), C::LDSK),
@@ -971,7 +963,6 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
               tta, M::ld(sDVnt + (16 * (ch * NCHB + m) + lr) * C::LDC + ks * KS + EPL * lg),
               dr[m]);
       }
-      __syncthreads();  // D block fully consumed before dR overwrites it
       {
       const f32x4 bet_s = row4(sbet), eg_s = row4(seg);
 #pragma unroll
@@ -983,8 +974,6 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
           const int s = 16 * rt + 4 * lg + i;
           const float x = dr[m][i];
           sDR[s * LDB + vc] = from_f32<E>(x);
-          // dk += (-beta e^g dR) S^T takes dR with its rows scaled
-          sDRs[s * LDB + vc] = from_f32<E>(-bet_s[i] * eg_s[i] * x);
           // dv = beta dR replaces this lane's own V elements (read above)
           sV[s * LDB + vc] = from_f32<E>(bet_s[i] * x);
           db_p[i] += x * (v4[i] - eg_s[i] * ks_[m][i]);
@@ -1003,6 +992,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
               *reinterpret_cast<const uint4 *>(sV + r * LDB + cv * VEC);
       }
       // ---- phase 6: dP += dO Vn^T, dA -= dR Vn^T, dk += (-beta e^g dR) S^T
+      // (the dR rows scaled in registers for the last)
+      const float dr_s = -sbet[ra] * seg[ra];
 #pragma unroll
       for (int ks = 0; ks < NKB; ++ks) {
         const auto doa = M::ld(sDO + ra * LDB + ks * KS + EPL * lg);
@@ -1014,7 +1005,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
             dp[cc] = M::mma(doa, vnb, dp[cc]);
             da[cc] = M::mma(dra, vnb, da[cc]);
           }
-        const auto drs = M::ld(sDRs + ra * LDB + ks * KS + EPL * lg);
+        const auto drs = M::scaled(dra, dr_s);
 #pragma unroll
         for (int m = 0; m < NCHK; ++m)
           dk[m] = M::mma(drs, M::ld_tr(sS + ks * KS * C::LDSK + 16 * (ch * NCHK + m), C::LDSK),

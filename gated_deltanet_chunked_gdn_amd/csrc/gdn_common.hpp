@@ -82,6 +82,13 @@ struct Mma<bf16> {
     for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)x[e] * wl[e]);
     return f;
   }
+  // a fragment with every element multiplied by s (rounded once)
+  __device__ static __forceinline__ frag scaled(const frag &x, float s) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)((float)x[e] * s);
+    return f;
+  }
   // X[m][k] + X[k][m]: 8 contiguous elements at p (as ld) plus the k-major
   // fragment of the same tile (rounded once)
   __device__ static __forceinline__ frag ld_sym_tr(const bf16 *p, const bf16 *tile, int pitch,
@@ -117,6 +124,7 @@ struct Mma<float> {
                                                       int l = threadIdx.x & 63) {
     return ld_tr(tile, ld, l) * w[l >> 4];
   }
+  __device__ static __forceinline__ frag scaled(frag x, float s) { return x * s; }
   __device__ static __forceinline__ frag ld_sym_tr(const float *p, const float *tile, int ld,
                                                    int l = threadIdx.x & 63) {
     return p[0] + ld_tr(tile, ld, l);
