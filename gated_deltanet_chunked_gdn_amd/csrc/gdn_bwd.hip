@@ -433,15 +433,17 @@ struct LocCfg {
   // row pitches: bf16 rows pad 32 bytes, which keeps their 16-byte fragment
   // reads free of bank conflicts; fp32 V-block rows and S/D rows pad 16
   // bytes (the fp32 footprint has no room for more)
-  static constexpr int PAD = 16 / (int)sizeof(E);
-  static constexpr int LDK = K + 32 / (int)sizeof(E);
-  static constexpr int LDC = 64 + 32 / (int)sizeof(E);
+  static constexpr int PAD = 16 / (int)sizeof(E);   // 16 bytes
+  static constexpr int PAD2 = 32 / (int)sizeof(E);  // 32 bytes
+  static constexpr int PADB = sizeof(E) == 2 ? PAD2 : PAD;
+  static constexpr int LDK = K + PAD2;
+  static constexpr int LDC = 64 + PAD2;
   static constexpr int VB = (sizeof(E) == 4) ? 32 : (V < 64 ? V : 64);
   static constexpr int NVB = V / VB;
-  static constexpr int LDB = VB + (sizeof(E) == 2 ? 16 : PAD);
+  static constexpr int LDB = VB + PADB;
   static constexpr int NCHB = VB / 32;  // V-block column tiles per half
   static constexpr int NCHK = K / 32;   // key column tiles per half
-  static constexpr int LDSK = K + (sizeof(E) == 2 ? 16 : PAD);  // rows of the transposed S and D blocks
+  static constexpr int LDSK = K + PADB;  // rows of the transposed S and D blocks
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + 64 * LDK;
   static constexpr int oT = oK + 64 * LDK;
