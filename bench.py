@@ -195,7 +195,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="hv64_t8192")
     ap.add_argument("--cp", type=int, default=-1, help="cp_mode (-1 automatic)")
-    ap.add_argument("--fwd-only", action="store_true", help="time the forward alone")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time the inference forward alone (o and the final state)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-state-cache", action="store_true",
                     help="the backward recomputes the per-chunk states instead of taking "
@@ -247,12 +248,13 @@ def main():
 
     def fwd(with_cache=use_cache):
         # with the cache the backward needs neither A nor g_cum (T and the
-        # states come from the cache), so the forward does not write them
+        # states come from the cache), so the forward does not write them;
+        # the forward alone is the inference forward (o and the final state)
         return gdn.chunk_gated_delta_rule_fwd(
             d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
             initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
             output_final_state=True, cp_mode=args.cp, return_states=False,
-            return_intermediates=not with_cache,
+            return_intermediates=not with_cache and not args.fwd_only,
             use_qk_l2norm_in_kernel=l2, state_cache=cache if with_cache else None)
 
     def bwd(A, with_cache=use_cache):
