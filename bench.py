@@ -39,10 +39,13 @@ def chunk_flops(K, V, n=CHUNK):
     """Algorithmic FLOPs of the chunked algorithm per full chunk per v-head.
 
     fwd = 2n^2(3K+2V) + 6nKV + n^3/3  (K K^T, Q K^T, w, u, w S, Q S, P Vn,
-    K^T Vn and the triangular inverse);  bwd = 2n^2(9K+5V) + 16nKV + 4n^3
-    (recompute plus every gradient product)."""
+    K^T Vn and the triangular inverse);  bwd = 2n^2(8K+5V) + 16nKV + 4n^3 +
+    n^3/3 (the recomputed K K^T, Q K^T, w, u, w S, Q S and inverse, plus
+    every gradient product: dVn, dK~, dP, dQ (two), dS (two), dw, dT (two),
+    dVb, dKb, dA (two n^3), dK (three)).  Every product is one the chunked
+    form performs; the inverse counts n^3/3."""
     fwd = 2 * n * n * (3 * K + 2 * V) + 6 * n * K * V + n ** 3 / 3
-    bwd = 2 * n * n * (9 * K + 5 * V) + 16 * n * K * V + 4 * n ** 3
+    bwd = 2 * n * n * (8 * K + 5 * V) + 16 * n * K * V + 4 * n ** 3 + n ** 3 / 3
     return fwd, bwd
 
 
