@@ -193,6 +193,8 @@ def _check_cache(cache, pr, q):
 
 
 def _check_inputs(q, k, v, g, beta):
+    """Shapes and dtypes of the forward inputs (the device is checked last,
+    by _check_device, after every other argument)."""
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B,T,Hq,K] and v [B,T,Hv,V]")
     if g.shape != v.shape[:3] or beta.shape != v.shape[:3]:
@@ -201,8 +203,22 @@ def _check_inputs(q, k, v, g, beta):
         raise TypeError("q, k, v and beta must share one dtype")
     if g.dtype != torch.float32:
         raise TypeError("g must be float32")
+
+
+def _check_state(x, name, shape):
+    """An optional fp32 state-shaped tensor ([N, Hv, K, V])."""
+    if x is not None and (x.dtype != torch.float32 or tuple(x.shape) != tuple(shape)):
+        raise ValueError(f"{name} must be float32 {list(shape)}, got "
+                         f"{x.dtype} {list(x.shape)}")
+
+
+def _check_device(q, *others):
+    """Every tensor on the GPU that holds q (a kernel reads each of them)."""
     if not q.is_cuda:
         raise ValueError("inputs must be on the GPU")
+    for x in others:
+        if x is not None and x.device != q.device:
+            raise ValueError(f"every tensor must be on {q.device}, got one on {x.device}")
 
 
 def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
@@ -229,8 +245,8 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     Hv, V = v.shape[2], v.shape[3]
     dev = q.device
     h0 = _contig(initial_state)
-    if h0 is not None and (h0.dtype != torch.float32 or tuple(h0.shape) != (pr.N, Hv, K, V)):
-        raise ValueError(f"initial_state must be float32 [{pr.N},{Hv},{K},{V}]")
+    _check_state(h0, "initial_state", (pr.N, Hv, K, V))
+    _check_device(q, k, v, g, beta, h0, state_cache)
     o = torch.empty_like(v)
     ht = torch.empty(pr.N, Hv, K, V, device=dev, dtype=torch.float32) if output_final_state else None
     g_cum = A = h = None
@@ -279,9 +295,19 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None,
     filled (the per-chunk states and T are then taken from it and A is not
     read), or None."""
     _check_inputs(q, k, v, g, beta)
+    if do is None or do.shape != v.shape or do.dtype != v.dtype:
+        raise ValueError(f"do must have v's shape {list(v.shape)} and dtype {v.dtype}")
     q, k, v, g, beta, do = (_contig(x) for x in (q, k, v, g, beta, do))
     A, dht, h0 = _contig(A), _contig(dht), _contig(initial_state)
     pr = _Prepared(q, v, scale, cu_seqlens, cp_mode, use_qk_l2norm_in_kernel)
+    B, T, Hq, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    if A is not None and (A.dtype != torch.float32 or tuple(A.shape) != (B, T, Hv, CHUNK)):
+        raise ValueError(f"A must be float32 [{B},{T},{Hv},{CHUNK}] (the forward's A), got "
+                         f"{A.dtype} {list(A.shape)}")
+    _check_state(dht, "dht", (pr.N, Hv, K, V))
+    _check_state(h0, "initial_state", (pr.N, Hv, K, V))
+    _check_device(q, k, v, g, beta, do, A, dht, h0, state_cache)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)

@@ -431,11 +431,12 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const vo
     return fail(GDN_ERR_INVALID_ARG,
                 "q, k, v, g, beta, do, dq, dk, dv, dbeta and dg are required");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(do_, 16) ||
-      !aligned(dq, 4) || !aligned(dk, 4) || !aligned(dv, 4) || !aligned(g, 4) ||
-      !aligned(A, 16) || !aligned(h0, 4) || !aligned(dht, 4) || !aligned(dh0, 4) ||
-      !aligned(dg, 4) || !aligned(state_cache, 16))
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(g, 4) ||
+      !aligned(dbeta, 4) || !aligned(A, 16) || !aligned(h0, 4) || !aligned(dht, 4) ||
+      !aligned(dh0, 4) || !aligned(dg, 4) || !aligned(state_cache, 16))
     return fail(GDN_ERR_LAYOUT,
-                "q, k, v, do, A, state_cache must be 16-byte aligned; fp32 buffers 4-byte");
+                "q, k, v, do, dq, dk, dv, A, state_cache must be 16-byte aligned; "
+                "dbeta and fp32 buffers 4-byte");
   const gdn::BwdWorkspace wl = bwd_layout(p, pl);
   if (!workspace || ws_bytes < wl.total)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,

@@ -37,14 +37,17 @@
  *   dv          [B, T, Hv, V], dbeta [B, T, Hv]: problem dtype; dg [B,T,Hv] fp32
  * With cu_seqlens, B must be 1, T is the total packed length and sequence n
  * covers tokens [cu[n], cu[n+1]); chunks never cross sequences.
- * Alignment: q, k, v, o, A, state_cache (forward) and q, k, v, do, A,
- * state_cache (backward) 16 bytes; every other buffer 4 bytes; the
- * workspace 256 bytes.
+ * Alignment: q, k, v, o, A, state_cache (forward) and q, k, v, do, dq, dk,
+ * dv, A, state_cache (backward) 16 bytes (they are read or written 16 bytes
+ * a lane); every other buffer 4 bytes; the workspace 256 bytes.
  *
- * Ownership: every buffer belongs to the caller.  The library allocates no
- * device memory; scratch comes from the caller's workspace (size from the
- * *_workspace_size calls, 256-byte aligned).  It keeps no state between
- * calls apart from the thread-local error message.
+ * Ownership: every buffer belongs to the caller.  The operator calls
+ * (gdn_chunk_fwd, gdn_chunk_bwd) allocate no device memory; their scratch
+ * comes from the caller's workspace (size from the *_workspace_size calls,
+ * 256-byte aligned).  The one exception in the library is the diagnostic
+ * gdn_selftest, which allocates, synchronises on and frees three small
+ * device buffers of its own.  The library keeps no state between calls
+ * apart from the thread-local error message.
  *
  * Asynchrony: work is enqueued on `stream` (a hipStream_t, NULL = default
  * stream) and the call returns without waiting for it.  No host
@@ -70,7 +73,7 @@ enum {
   GDN_OK = 0,
   GDN_ERR_INVALID_ARG = 1, /* null required pointer, bad dims, bad cu_seqlens */
   GDN_ERR_UNSUPPORTED = 2, /* Hv % Hq != 0, K or V not in {32, 64, 128}, dtype */
-  GDN_ERR_LAYOUT = 3,      /* pointer not aligned to 16 bytes */
+  GDN_ERR_LAYOUT = 3,      /* pointer not aligned as documented below */
   GDN_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned */
   GDN_ERR_HIP = 5          /* a HIP launch or runtime call failed */
 };
@@ -155,7 +158,9 @@ const char *gdn_last_error(void);
 
 /* Runs the library's MFMA lane-layout self-check on the current device:
  * 0 when the bf16 and fp32 matrix instructions give the products the
- * kernels assume, GDN_ERR_HIP otherwise (synchronous; diagnostics only). */
+ * kernels assume, GDN_ERR_HIP otherwise.  Diagnostics only: unlike the
+ * operator calls it allocates (and frees) its own small device buffers and
+ * waits for the device before it returns. */
 int gdn_selftest(void);
 
 #ifdef __cplusplus

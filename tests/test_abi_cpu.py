@@ -111,6 +111,20 @@ def test_bwd_validation():
     assert rc == 1  # dq missing
 
 
+@pytest.mark.parametrize("slot", [10, 11, 12])  # dq, dk, dv
+def test_bwd_gradient_outputs_need_16_byte_alignment(slot):
+    """dq, dk and dv leave the kernels as 16-byte row pieces."""
+    p = prob()
+    L = gdn.lib()
+    P = ctypes.c_void_p
+    args = [P(16)] * 16
+    args[5] = args[6] = args[8] = args[14] = args[15] = None  # A, h0, dht, dh0, cache
+    args[slot - 1] = P(24)
+    rc = L.gdn_chunk_bwd(ctypes.byref(p), *args, P(1 << 20), 1 << 30, None)
+    assert rc == 3, gdn.last_error()
+    assert "16-byte" in gdn.last_error()
+
+
 def test_plan_segments_cp_modes():
     L = gdn.lib()
     p = prob(T=8192, Hv=64, Hq=32)
