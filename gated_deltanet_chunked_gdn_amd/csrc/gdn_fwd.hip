@@ -35,6 +35,8 @@
 //          writes the final state H_last + rho.  Every step is exact by
 //          linearity of the recurrence in the state, up to the dropped
 //          denormal remainders.
+#include <stdlib.h>
+
 #include "gdn_seg.hpp"
 
 namespace gdn {
@@ -908,6 +910,16 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
   prep_kernel<E, K><<<dim3((unsigned)grid), kPrepThreads, lds, st>>>(a);
 }
 
+// GDN_FWD_SLICE=0 in the environment runs pass 1 on the general segment
+// kernel even where the register-resident one applies (for comparisons).
+static bool slice_disabled() {
+  static const bool off = [] {
+    const char *e = getenv("GDN_FWD_SLICE");
+    return e && e[0] == '0';
+  }();
+  return off;
+}
+
 // Stage bits of launch_fwd_t: the plan prefix sums and prep (T from k or
 // from a given A), then the segment passes.
 constexpr int kStagePlan = 1, kStageT = 2, kStageSegs = 4;
@@ -925,7 +937,10 @@ static hipError_t launch_fwd_t(const FwdArgs &a, const float *Ain, hipStream_t s
   if ((stages & kStageT) && pl.total_chunks > 0) launch_prep<E, K>(a, Ain, st);
   if (!(stages & kStageSegs)) return hipGetLastError();
   if (pl.total_chunks > 0) {
-    {
+    if (WRITE_O && fwd_slice_supported(a) && !slice_disabled()) {
+      const hipError_t e = launch_fwd_slice_main(a, st);
+      if (e != hipSuccess) return e;
+    } else {
       KernelTimer kt(WRITE_O ? "fwd_main" : "state_main", st);
       segment_kernel<E, K, V, kMain, WRITE_O>
           <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);

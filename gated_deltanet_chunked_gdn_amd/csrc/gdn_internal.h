@@ -87,6 +87,10 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+// pass 1 of the forward with the recurrence in registers (gdn_fwd_slice.hip):
+// bf16, K = V = 128
+bool fwd_slice_supported(const FwdArgs &a);
+hipError_t launch_fwd_slice_main(const FwdArgs &a, hipStream_t stream);
 // states only (a.h), no output; T from Ain ([B,T,Hv,64] fp32) when given
 hipError_t launch_bwd_prep(const FwdArgs &a, const float *Ain, hipStream_t stream);
 hipError_t launch_fwd_states(const FwdArgs &a, hipStream_t stream);

@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_util import TOL, announce, oracle_bwd, rel, to_dev, token_mask
+from tests.gpu_util import (BLOCK_TOL, BLOCK_TOL_CANCEL, TOL, announce, block_rel_max,
+                            oracle_bwd, rel, to_dev, token_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,17 +117,25 @@ def _sampled_bwd(gdn, heads, gate="default", T=None, cp=-1):
     grp = w.Hv // w.Hq
     qk_heads = sorted({h // grp for h in heads})
     tm = token_mask(p, mask)
-    errs = {}
+    errs, blocks = {}, {}
     for n, x, r in zip(NAMES, got, ref):
         x = x.double().cpu().numpy()
         if n in ("dq", "dk"):
             errs[n] = rel(x[:, :, qk_heads], r[:, :, qk_heads])
+            blocks[n] = block_rel_max(x[:, :, qk_heads], r[:, :, qk_heads])
         elif n == "dh0":
             errs[n] = rel(x[mask], r[mask])
+            blocks[n] = max(rel(x[b, hh], r[b, hh]) for b, hh in zip(*np.nonzero(mask)))
         else:
             errs[n] = rel(x[tm], r[tm])
+            blocks[n] = block_rel_max(x, r, tm)
+    announce("  rel " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) +
+             " | worst block " + " ".join(f"{n}={e:.2e}" for n, e in blocks.items()))
     bad = {n: e for n, e in errs.items() if not e <= TOL[w.dtype]}
     assert not bad, f"{bad} (all {errs})"
+    btol = {n: (BLOCK_TOL_CANCEL if n in ("db", "dg") else BLOCK_TOL)[w.dtype] for n in NAMES}
+    bad = {n: e for n, e in blocks.items() if not e <= btol[n]}
+    assert not bad, f"worst 64-token block: {bad} (all {blocks})"
 
 
 def test_full_bwd_b2_t16384_hv16(gdn):

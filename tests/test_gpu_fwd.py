@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_util import TOL, announce, oracle_fwd, rel, to_dev, token_mask
+from tests.gpu_util import (BLOCK_TOL, TOL, announce, block_rel_max, oracle_fwd, rel,
+                            to_dev, token_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,10 +106,14 @@ def test_cp_split_agrees_with_unsplit_and_is_deterministic(gdn):
     assert torch.equal(oa, ob) and torch.equal(ha, hb)
 
 
-def test_intermediates_gate_cumsum_and_inverse(gdn):
-    """g_cum and A against the oracle's chunked intermediates (fp64)."""
+@pytest.mark.parametrize("gate", ["default", "slow", "nodecay"])
+def test_intermediates_gate_cumsum_and_inverse(gdn, gate):
+    """g_cum, A and the per-chunk states h against the oracle's chunked
+    intermediates (fp64).  With one chunk per segment (cp_mode=1) every h
+    after the first passes through the fix-up and serial carry; the slow and
+    no-decay gates keep those corrections large."""
     from oracle import chunked
-    p = synth.custom(1, 150, 1, 2, 64, 64, dtype="f32", seed=2, gate="default")
+    p = synth.custom(1, 150, 1, 2, 64, 64, dtype="f32", seed=2, gate=gate)
     g_cum, A, o, h, ht = run_fwd(gdn, p, cp_mode=1, want_inter=True)
     q, k, v, g, b = (p[n][0].double().numpy() for n in ("q", "k", "v", "g", "beta"))
     for hh in range(2):
@@ -137,8 +142,15 @@ def _sampled(gdn, name, heads, gate="default", T=None, cp=-1):
     o_np = o.double().cpu().numpy()
     eo = rel(o_np[tm], ro[tm])
     eh = rel(ht.double().cpu().numpy()[mask], rht[mask])
+    # per 64-token block of each sampled head, and per (sequence, head) state
+    bo = block_rel_max(o_np, ro, tm)
+    ht_np = ht.double().cpu().numpy()
+    bh = max(rel(ht_np[n, hh], rht[n, hh]) for n, hh in zip(*np.nonzero(mask)))
+    announce(f"  o rel {eo:.2e} (worst block {bo:.2e}), final {eh:.2e} (worst unit {bh:.2e})")
     assert eo <= TOL[w.dtype], f"{name} o rel err {eo:.3e}"
     assert eh <= TOL[w.dtype], f"{name} final rel err {eh:.3e}"
+    assert bo <= BLOCK_TOL[w.dtype], f"{name} o worst 64-token block rel err {bo:.3e}"
+    assert bh <= BLOCK_TOL[w.dtype], f"{name} worst final state rel err {bh:.3e}"
     assert np.isfinite(o_np).all()
 
 
@@ -159,6 +171,12 @@ def test_hv8_long_slow_decay_cp_fixup(gdn):
     _sampled(gdn, "hv8_t65536", heads=[3], gate="slow", T=16384)
 
 
+def test_hv8_t65536_full_length_slow_decay(gdn):
+    # the whole 65536-token sequence (1024 chunks, every segment boundary of
+    # the automatic split) with a state that survives many chunks
+    _sampled(gdn, "hv8_t65536", heads=[3], gate="slow")
+
+
 def test_hv8_long_no_decay(gdn):
     _sampled(gdn, "hv8_t65536", heads=[2], gate="nodecay", T=8192)
 
@@ -169,3 +187,30 @@ def test_full_varlen16_hv32(gdn):
 
 def test_full_varlen16_hv32_slow(gdn):
     _sampled(gdn, "varlen16_hv32", heads=[7], gate="slow")
+
+
+@pytest.mark.parametrize("dtype,K,V,T,T1", [("bf16", 128, 128, 3000, 1234),
+                                            ("bf16", 64, 64, 700, 64),
+                                            ("f32", 32, 32, 400, 130)])
+def test_resume_invariance(gdn, dtype, K, V, T, T1):
+    """[0, T1) then [T1, T) with the first call's final state as the second
+    call's initial state equals one call over [0, T)."""
+    p = synth.custom(2, T, 2, 4, K, V, dtype=dtype, seed=31, gate="slow", h0=True)
+    d = to_dev(p)
+    announce(f"resume {dtype} K={K} V={V} T={T} T1={T1}")
+
+    def fwd(sl, h0):
+        q, k, v, g, b = (d[n][:, sl].contiguous() for n in ("q", "k", "v", "g", "beta"))
+        return gdn.chunk_gated_delta_rule(q, k, v, g, b, scale=d["scale"], initial_state=h0,
+                                          output_final_state=True)
+
+    o, ht = fwd(slice(0, T), d["initial_state"])
+    o1, h1 = fwd(slice(0, T1), d["initial_state"])
+    o2, h2 = fwd(slice(T1, T), h1)
+    torch.cuda.synchronize()
+    o12 = torch.cat([o1, o2], dim=1).double().cpu().numpy()
+    ref = o.double().cpu().numpy()
+    assert rel(o12, ref) <= TOL[dtype]
+    assert rel(h2, ht.double().cpu().numpy()) <= TOL[dtype]
+    ro, rht = oracle_fwd(p)
+    assert rel(o12, ro) <= TOL[dtype] and rel(h2, rht) <= TOL[dtype]

@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_util import TOL, announce, oracle_bwd, oracle_fwd, rel, to_dev, token_mask
+from tests.gpu_util import (BLOCK_TOL, BLOCK_TOL_CANCEL, TOL, announce, block_rel_max,
+                            oracle_bwd, oracle_fwd, rel, to_dev, token_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,8 +100,10 @@ def test_cache_matches_recompute_and_oracle(gdn, case):
     p = build()
     got, rec = both(gdn, p, cp, l2)
     for n, x, y in zip(NAMES, got, rec):
-        # the same passes produce the same states: equal up to rounding order
-        assert rel(x.float().cpu().numpy(), y.float().cpu().numpy()) <= 1e-6, n
+        # the cached states come from the forward's pass 1 and the recomputed
+        # ones from the backward's state pass: two kernels, one recurrence, so
+        # the gradients agree to the rounding of the bf16 states
+        assert rel(x.float().cpu().numpy(), y.float().cpu().numpy()) <= TOL[dtype], n
     ref = oracle_bwd(p) if not l2 else None
     if ref is not None:
         errs = {n: rel(x, r) for n, x, r in zip(NAMES, got, ref)}
@@ -132,8 +135,10 @@ def test_full_hv64_t8192_cached_step(gdn):
     mask[:, heads] = True
     tm = token_mask(p, mask)
     ro, rht = oracle_fwd(p, unit_mask=mask)
-    errs = {"o": rel(o.double().cpu().numpy()[tm], ro[tm]),
+    o_np = o.double().cpu().numpy()
+    errs = {"o": rel(o_np[tm], ro[tm]),
             "ht": rel(ht.double().cpu().numpy()[mask], rht[mask])}
+    blocks = {"o": block_rel_max(o_np, ro, tm)}
     ref = oracle_bwd(p, unit_mask=mask)
     grp = w.Hv // w.Hq
     qk_heads = sorted({h // grp for h in heads})
@@ -142,9 +147,16 @@ def test_full_hv64_t8192_cached_step(gdn):
         assert np.isfinite(x).all(), n
         if n in ("dq", "dk"):
             errs[n] = rel(x[:, :, qk_heads], r[:, :, qk_heads])
+            blocks[n] = block_rel_max(x[:, :, qk_heads], r[:, :, qk_heads])
         elif n == "dh0":
             errs[n] = rel(x[mask], r[mask])
         else:
             errs[n] = rel(x[tm], r[tm])
+            blocks[n] = block_rel_max(x, r, tm)
+    announce("  rel " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) +
+             " | worst block " + " ".join(f"{n}={e:.2e}" for n, e in blocks.items()))
     bad = {n: e for n, e in errs.items() if not e <= TOL[w.dtype]}
     assert not bad, f"{bad} (all {errs})"
+    btol = {n: (BLOCK_TOL_CANCEL if n in ("db", "dg") else BLOCK_TOL)[w.dtype] for n in blocks}
+    bad = {n: e for n, e in blocks.items() if not e <= btol[n]}
+    assert not bad, f"worst 64-token block: {bad} (all {blocks})"
