@@ -92,11 +92,11 @@ struct Item {
 
 // ------------------------------------------------------------------ helpers
 // Helper wave roles (HW = wave - 4):
-//   0  q, k rows 0..31 into LDS; P tile (rows 0..31, columns 0..31)
+//   0  q, k and T rows 0..31 into LDS; P tile (rows 0..31, columns 0..31)
 //   1  the previous chunk's output rows out of LDS, then v rows into the
 //      same LDS rows (one wave, so the reads come before the writes)
-//   2  q, k rows 32..63 into LDS; P tile (rows 32..63, columns 32..63)
-//   3  T, the gates; P tile (rows 32..63, columns 0..31)
+//   2  q, k and T rows 32..63 into LDS; P tile (rows 32..63, columns 32..63)
+//   3  the gates; P tile (rows 32..63, columns 0..31)
 // (P is lower triangular: its tile (rows 0..31, columns 32..63) is zero and
 // never read.)  Every role loads the rows it needs itself, so the helpers
 // never wait for one another.  Loads are issued a chunk and a half before
@@ -105,11 +105,11 @@ struct Item {
 constexpr bool has_qk(int hw) { return hw != 1; }
 template <int HW>
 struct HelperRegs {
-  static constexpr int NB = HW == 1 ? 16 : (HW == 3 ? 24 : 16);  // 16-byte pieces
+  static constexpr int NB = (HW == 0 || HW == 2) ? 20 : 16;  // 16-byte pieces
   // roles 0, 2, 3: k rows (buf[0..7]) and q rows (buf[8..15]) of the P tile,
   // rho-ordered 8-byte pairs (slot s holds columns 16 s + 4 h + [0..3] and
-  // 16 s + 8 + 4 h + [0..3]); role 3 also T rows (buf[16..23]); role 1: v
-  // rows (buf[0..15]); 16-byte pieces of T and v in natural order
+  // 16 s + 8 + 4 h + [0..3]); roles 0, 2 also half the T rows (buf[16..19]);
+  // role 1: v rows (buf[0..15]); 16-byte pieces of T and v in natural order
   uint4 buf[NB];
   float g;
   float b;
@@ -161,13 +161,14 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const FwdArgs &a,
       R.buf[m] = bload16(rv, (uint32_t)r * rs + 16u * pc);
     }
   }
-  if (HW == 3) {
+  if (HW == 0 || HW == 2) {
+    // T rows 0..31 (role 0) or 32..63 (role 2): 8 16-byte pieces a row
     const int64_t cgid = it.sl.chunk0 + c;
     const uint4 *tb = reinterpret_cast<const uint4 *>(
         reinterpret_cast<const bf16 *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat) +
         (cgid * p.Hv + it.h) * 64 * 64);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) R.buf[16 + m] = tb[lane + 64 * m];
+    for (int m = 0; m < 4; ++m) R.buf[16 + m] = tb[lane + 64 * (m + 2 * HW)];
   }
   // every role keeps the chunk's gates (P needs gamma); rows past the end: 0
   const uint32_t gs = (uint32_t)(p.Hv * 4);
@@ -231,17 +232,20 @@ __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set
       *reinterpret_cast<uint4 *>(set + oV + r * PITCH + 8 * pc) = R.buf[m];
     }
   }
-  if (HW == 3) {
-    // T rows (pi layout), gates
+  if (HW == 0 || HW == 2) {
+    // T rows (pi layout)
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int idx = lane + 64 * m, r = idx >> 3, pc = idx & 7;  // 8 columns 8 pc ..
-      const int c0 = 8 * pc, blk = c0 & ~15, q0 = (c0 >> 2) & 3;   // groups q0, q0 + 1
+    for (int m = 0; m < 4; ++m) {
+      const int idx = lane + 64 * (m + 2 * HW), r = idx >> 3, pc = idx & 7;  // columns 8 pc ..
+      const int c0 = 8 * pc, blk = c0 & ~15, q0 = (c0 >> 2) & 3;  // groups q0, q0 + 1
       bf16 *row = set + oT + r * PITCH_C + blk;
       const uint4 t = R.buf[16 + m];
       *reinterpret_cast<uint2 *>(row + 4 * pi4(q0)) = make_uint2(t.x, t.y);
       *reinterpret_cast<uint2 *>(row + 4 * pi4(q0 + 1)) = make_uint2(t.z, t.w);
     }
+  }
+  if (HW == 3) {
+    // the gates
     const float gL = lane63(gam);
     const float eg = __builtin_amdgcn_exp2f(gam);
     gates[gGam + lane] = gam;
