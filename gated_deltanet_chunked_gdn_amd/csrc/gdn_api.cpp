@@ -342,7 +342,7 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p) {
   return bwd_layout(p, pl).total;
 }
 
-// State cache layout: the per-chunk states ([chunks][Hv][V][K], element
+// State cache layout: the per-chunk states ([chunks][Hv][K*V] in the lane layout, element
 // type), then at a 256-byte boundary the per-chunk T ([chunks][Hv][64][64]).
 static size_t cache_t_offset(const gdn_problem_t *p, const gdn::Plan &pl) {
   const size_t es = p->dtype == GDN_BF16 ? 2 : 4;

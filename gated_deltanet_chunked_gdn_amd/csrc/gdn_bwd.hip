@@ -623,17 +623,27 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     const int h = x.hq * Gq + hl;
     const int64_t cg = x.gid * p.Hv + h;
     const int v0 = vb * VB;
-    // rows v0 .. v0 + VB - 1 of the transposed states: one contiguous block
+    // columns v0 .. v0 + VB - 1 of the states: one contiguous block of the
+    // lane layout (S) and rows v0 .. of the transposed gradients (D); each
+    // piece of D is gathered to hold the same elements as its piece of S
     const char *hsb = reinterpret_cast<const char *>(hst + cg * (int64_t)K * V + v0 * K);
-    const char *dsb = reinterpret_cast<const char *>(dst + cg * (int64_t)K * V + v0 * K);
+    const E *dsb = dst + cg * (int64_t)K * V + v0 * K;
 #pragma unroll
     for (int m = 0; m < LP::NSP; ++m) {
       const int idx = tid + kThreads * m;
       uint4 zs = make_uint4(0u, 0u, 0u, 0u), zd = zs;
       if (idx < VB * LP::PK) {
-        const uint32_t off = (uint32_t)idx * 16u;
-        zs = *reinterpret_cast<const uint4 *>(hsb + off);
-        zd = *reinterpret_cast<const uint4 *>(dsb + off);
+        zs = *reinterpret_cast<const uint4 *>(hsb + (uint32_t)idx * 16u);
+        int r, k_lo, k_hi;
+        if (sizeof(E) == 2) {
+          lane_unit<K>(idx, r, k_lo, k_hi);
+          const uint2 a = *reinterpret_cast<const uint2 *>(dsb + r * K + k_lo);
+          const uint2 b = *reinterpret_cast<const uint2 *>(dsb + r * K + k_hi);
+          zd = make_uint4(a.x, a.y, b.x, b.y);
+        } else {
+          lane_unit<K>(idx >> 1, r, k_lo, k_hi);
+          zd = *reinterpret_cast<const uint4 *>(dsb + r * K + ((idx & 1) ? k_hi : k_lo));
+        }
       }
       pf.s[m] = zs;
       pf.d[m] = zd;
@@ -790,10 +800,21 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
         for (int m = 0; m < LP::NSP; ++m) {
           const int idx = tid + kThreads * m;
           if (idx < VB * LP::PK) {
-            const int r = idx / LP::PK, cv = idx % LP::PK;
             gl_p = dot_piece<E>(pf.s[m], pf.d[m], gl_p);
-            *reinterpret_cast<uint4 *>(sS + r * C::LDSK + cv * VEC) = pf.s[m];
-            *reinterpret_cast<uint4 *>(sD + r * C::LDSK + cv * VEC) = pf.d[m];
+            int r, k_lo, k_hi;
+            if (sizeof(E) == 2) {
+              lane_unit<K>(idx, r, k_lo, k_hi);
+              const uint4 x = pf.s[m], y = pf.d[m];
+              *reinterpret_cast<uint2 *>(sS + r * C::LDSK + k_lo) = make_uint2(x.x, x.y);
+              *reinterpret_cast<uint2 *>(sS + r * C::LDSK + k_hi) = make_uint2(x.z, x.w);
+              *reinterpret_cast<uint2 *>(sD + r * C::LDSK + k_lo) = make_uint2(y.x, y.y);
+              *reinterpret_cast<uint2 *>(sD + r * C::LDSK + k_hi) = make_uint2(y.z, y.w);
+            } else {
+              lane_unit<K>(idx >> 1, r, k_lo, k_hi);
+              const int k0 = (idx & 1) ? k_hi : k_lo;
+              *reinterpret_cast<uint4 *>(sS + r * C::LDSK + k0) = pf.s[m];
+              *reinterpret_cast<uint4 *>(sD + r * C::LDSK + k0) = pf.d[m];
+            }
           }
         }
 #pragma unroll

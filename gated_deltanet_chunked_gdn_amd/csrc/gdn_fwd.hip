@@ -539,7 +539,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       float *hs = a.h + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
       tiles_store<E, K, V>(st, hs, nullptr, MODE == kFix, tid);
     }
-    // per-chunk states (transposed): pass 1 stores the LDS mirror written
+    // per-chunk states (lane layout): pass 1 stores the LDS mirror written
     // last step; the fix-up pass adds its correction, reading the stored
     // values here and writing the sums after phase A
     E *hs = a.h_e ? reinterpret_cast<E *>(a.h_e) + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V
@@ -563,9 +563,9 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
     TilesOld<E, K, V> hold;
     if (hs) {
       if (MODE == kFix)
-        tiles_old_t<E, K, V>(hold, hs, tid);
+        tiles_old_l<E, K, V>(hold, hs, tid);
       else
-        mirror_store_t<E, K, V>(sSt, hs, tid);
+        mirror_store_l<E, K, V>(sSt, hs, tid);
     }
     // the next chunk's inputs travel while this whole chunk is computed (this
     // chunk's inputs were committed to LDS at the end of the previous one)
@@ -619,7 +619,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
         }
       }
     }
-    if (MODE == kFix && hs) tiles_accumulate_t<E, K, V>(st, hold, hs, tid);
+    if (MODE == kFix && hs) tiles_accumulate_l<E, K, V>(st, hold, hs, tid);
     float eg_r[4], b_r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

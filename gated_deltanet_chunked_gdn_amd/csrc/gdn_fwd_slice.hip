@@ -98,30 +98,30 @@ struct Item {
 //   2  q, k and T rows 32..63 into LDS; P tile (rows 32..63, columns 32..63)
 //   3  the gates; P tile (rows 32..63, columns 0..31)
 // (P is lower triangular: its tile (rows 0..31, columns 32..63) is zero and
-// never read.)  Every role loads the rows it needs itself, so the helpers
-// never wait for one another.  Loads are issued a chunk and a half before
+// never read.)  Rows are loaded whole (16 consecutive lanes cover one
+// 256-byte row) and each P tile reads its operands back from the LDS rows
+// its own wave has just written: role 3 writes the q rows 32..63 and k rows
+// 0..31 it needs itself, the same bytes roles 2 and 0 write there, so no
+// helper ever waits for another.  Loads are issued a chunk and a half before
 // their data is committed: the registers hold two chunks, and loads past the
 // end of a sequence return zeros (buffer range), so no load is conditional.
-constexpr bool has_qk(int hw) { return hw != 1; }
 template <int HW>
 struct HelperRegs {
-  static constexpr int NB = (HW == 0 || HW == 2) ? 20 : 16;  // 16-byte pieces
-  // roles 0, 2, 3: k rows (buf[0..7]) and q rows (buf[8..15]) of the P tile,
-  // rho-ordered 8-byte pairs (slot s holds columns 16 s + 4 h + [0..3] and
-  // 16 s + 8 + 4 h + [0..3]); roles 0, 2 also half the T rows (buf[16..19]);
-  // role 1: v rows (buf[0..15]); 16-byte pieces of T and v in natural order
+  // roles 0, 2, 3: q rows (buf[0..7]) and k rows (buf[8..15]) of one half of
+  // the chunk, 16-byte piece lane & 15 of row 4 m + (lane >> 4); roles 0, 2
+  // also 4 pieces of T (buf[16..19]); role 1: v rows (buf[0..15])
+  static constexpr int NB = (HW == 0 || HW == 2) ? 20 : 16;
   uint4 buf[NB];
   float g;
   float b;
 };
+// q rows of role HW: 0..31 (role 0) or 32..63; k rows: 32..63 (role 2) or 0..31
+__device__ __forceinline__ constexpr int q_half(int hw) { return hw == 0 ? 0 : 1; }
+__device__ __forceinline__ constexpr int k_half(int hw) { return hw == 2 ? 1 : 0; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
-}
-__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-  return make_uint2(x[0], x[1]);
 }
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
@@ -135,31 +135,25 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const FwdArgs &a,
   const Problem &p = a.p;
   const int64_t tok0 = it.sl.si.tok0 + (int64_t)c * kChunk;
   const int rows = min(kChunk, it.sl.si.len - c * kChunk);
-  const int h = lane >> 5, r32 = lane & 31;
-  if (has_qk(HW)) {
-    constexpr int rbq = HW == 0 ? 0 : 1, rbk = HW == 2 ? 1 : 0;
+  const int r16 = lane >> 4, pc = lane & 15;
+  if (HW != 1) {
     const uint32_t rs = (uint32_t)(p.Hq * K * 2);  // bytes between token rows
     const bf16 *qb = reinterpret_cast<const bf16 *>(a.q) + (tok0 * p.Hq + it.hq) * K;
     const bf16 *kb = reinterpret_cast<const bf16 *>(a.k) + (tok0 * p.Hq + it.hq) * K;
     const auto rq = rsrc_of(qb, (uint32_t)rows * rs), rk = rsrc_of(kb, (uint32_t)rows * rs);
-    const uint32_t oq = (uint32_t)(32 * rbq + r32) * rs + 8u * h;
-    const uint32_t ok = (uint32_t)(32 * rbk + r32) * rs + 8u * h;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint2 q0 = bload8(rq, oq + 32u * s), q1 = bload8(rq, oq + 32u * s + 16u);
-      const uint2 k0 = bload8(rk, ok + 32u * s), k1 = bload8(rk, ok + 32u * s + 16u);
-      R.buf[8 + s] = make_uint4(q0.x, q0.y, q1.x, q1.y);
-      R.buf[s] = make_uint4(k0.x, k0.y, k1.x, k1.y);
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t rq0 = (uint32_t)(32 * q_half(HW) + 4 * m + r16);
+      const uint32_t rk0 = (uint32_t)(32 * k_half(HW) + 4 * m + r16);
+      R.buf[m] = bload16(rq, rq0 * rs + 16u * pc);
+      R.buf[8 + m] = bload16(rk, rk0 * rs + 16u * pc);
     }
   } else {
     const uint32_t rs = (uint32_t)(p.Hv * V * 2);
     const bf16 *vb = reinterpret_cast<const bf16 *>(a.v) + (tok0 * p.Hv + it.h) * V;
     const auto rv = rsrc_of(vb, (uint32_t)rows * rs);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int idx = lane + 64 * m, r = idx >> 4, pc = idx & 15;
-      R.buf[m] = bload16(rv, (uint32_t)r * rs + 16u * pc);
-    }
+    for (int m = 0; m < 16; ++m) R.buf[m] = bload16(rv, (uint32_t)(4 * m + r16) * rs + 16u * pc);
   }
   if (HW == 0 || HW == 2) {
     // T rows 0..31 (role 0) or 32..63 (role 2): 8 16-byte pieces a row
@@ -181,35 +175,48 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const FwdArgs &a,
   R.b = (float)__builtin_bit_cast(bf16, braw);
 }
 
+// A 16-byte piece holding columns 8 pc .. 8 pc + 7 of a row, written into a
+// pi-layout row: its two 4-column groups go to their swapped positions.
+__device__ __forceinline__ void put_pi(bf16 *row, int pc, const uint4 &x) {
+  const int blk = (8 * pc) & ~15, q0 = 2 * (pc & 1);
+  *reinterpret_cast<uint2 *>(row + blk + 4 * pi4(q0)) = make_uint2(x.x, x.y);
+  *reinterpret_cast<uint2 *>(row + blk + 4 * pi4(q0 + 1)) = make_uint2(x.z, x.w);
+}
+
 // Writes the chunk held in R into buffer set `set` (role HW's share).
 template <int HW>
 __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set, float *gates,
                                               float *scratch, int lane) {
-  const int h = lane >> 5, r32 = lane & 31;
+  const int h = lane >> 5, r32 = lane & 31, r16 = lane >> 4, pc = lane & 15;
   const float gam = wave_incl_scan(R.g) * kLog2e;  // gate cumsum, times log2(e)
-  if (has_qk(HW)) {
-    constexpr int rbq = HW == 0 ? 0 : 1, rbk = HW == 2 ? 1 : 0;
+  if (HW != 1) {
+    constexpr int rbq = q_half(HW), rbk = k_half(HW);
     float *sg = scratch + 64 * (HW == 3 ? 1 : HW);  // this wave's own copy of gamma
     sg[lane] = gam;
-    if (HW != 3) {
-      // q and k rows into the pi layout: one 16-byte piece per slot
-      bf16 *dq = set + oQ + (32 * rbq + r32) * PITCH + 8 * h;
-      bf16 *dk = set + oK + (32 * rbk + r32) * PITCH + 8 * h;
+    // q and k rows of this half into the pi layout
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        *reinterpret_cast<uint4 *>(dq + 16 * s) = R.buf[8 + s];
-        *reinterpret_cast<uint4 *>(dk + 16 * s) = R.buf[s];
+    for (int m = 0; m < 8; ++m) {
+      put_pi(set + oQ + (32 * rbq + 4 * m + r16) * PITCH, pc, R.buf[m]);
+      put_pi(set + oK + (32 * rbk + 4 * m + r16) * PITCH, pc, R.buf[8 + m]);
+    }
+    if (HW != 3) {
+      // T rows (pi layout)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int idx = lane + 64 * (m + 2 * HW);  // 16-byte piece of T
+        put_pi(set + oT + (idx >> 3) * PITCH_C, idx & 7, R.buf[16 + m]);
       }
     }
-    // P^T tile: rows j (k rows 32 rbk..), columns r (q rows 32 rbq..)
-    f32x16 acc = zero16();
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      acc = mma32(__builtin_bit_cast(bf16x8, R.buf[s]), __builtin_bit_cast(bf16x8, R.buf[8 + s]),
-                  acc);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // P^T tile: rows j (k rows 32 rbk..), columns r (q rows 32 rbq..), from
+    // the rows just written (rho-ordered slots of both operands)
+    const bf16 *ka = set + oK + (32 * rbk + r32) * PITCH + 8 * h;
+    const bf16 *qa = set + oQ + (32 * rbq + r32) * PITCH + 8 * h;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = mma32(lds16(ka + 16 * s), lds16(qa + 16 * s), acc);
     const int r = 32 * rbq + r32;  // this lane's output row (token) of P
     const float gr = sg[r];
     bf16 *prow = set + oP + r * PITCH_C;
@@ -227,22 +234,8 @@ __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set
   } else {
     // v rows (natural layout)
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int idx = lane + 64 * m, r = idx >> 4, pc = idx & 15;
-      *reinterpret_cast<uint4 *>(set + oV + r * PITCH + 8 * pc) = R.buf[m];
-    }
-  }
-  if (HW == 0 || HW == 2) {
-    // T rows (pi layout)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int idx = lane + 64 * (m + 2 * HW), r = idx >> 3, pc = idx & 7;  // columns 8 pc ..
-      const int c0 = 8 * pc, blk = c0 & ~15, q0 = (c0 >> 2) & 3;  // groups q0, q0 + 1
-      bf16 *row = set + oT + r * PITCH_C + blk;
-      const uint4 t = R.buf[16 + m];
-      *reinterpret_cast<uint2 *>(row + 4 * pi4(q0)) = make_uint2(t.x, t.y);
-      *reinterpret_cast<uint2 *>(row + 4 * pi4(q0 + 1)) = make_uint2(t.z, t.w);
-    }
+    for (int m = 0; m < 16; ++m)
+      *reinterpret_cast<uint4 *>(set + oV + (4 * m + r16) * PITCH + 8 * pc) = R.buf[m];
   }
   if (HW == 3) {
     // the gates
@@ -330,8 +323,8 @@ struct ChainCtx {
 // One chunk of chain wave j on buffer set `set` (gates `gt`): S (4 tiles,
 // rows 32 m .. of K, columns 32 j .. of V) advances by one chunk and the
 // chunk's output slice is staged (scaled, bf16) in the v rows of the set.
-// `hcache` (nullable) receives the entering state, bf16, transposed (row v,
-// column k).
+// `hcache` (nullable) receives the entering state, bf16, in the lane layout
+// of the state cache (gdn_seg.hpp).
 //
 // With one chain wave per SIMD the wave's own instruction stream has to hide
 // the LDS latency: every operand fragment is read one or two product groups
@@ -376,11 +369,9 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
     GDN_FENCE();
     const bf16x8 sb = slots(S[s >> 1], s & 1);
     if (hcache) {
-      // row v = 32 j + r32 of S^T: slot e of k-step s is column 16 s + rho(h, e)
-      const uint4 u = __builtin_bit_cast(uint4, sb);
-      bf16 *row = hcache + (32 * j + r32) * K + 4 * h + 16 * s;
-      *reinterpret_cast<uint2 *>(row) = make_uint2(u.x, u.y);
-      *reinterpret_cast<uint2 *>(row + 8) = make_uint2(u.z, u.w);
+      // the lane layout of the state cache is these very slots: one whole
+      // 1 KB piece per k-step and wave
+      *reinterpret_cast<bf16x8 *>(hcache + ((j * 8 + s) * 64 + lane) * 8) = sb;
     }
     const bf16x8(&f)[4] = F[s % 3];
     KS[0] = mma32(f[0], sb, KS[0]);
@@ -450,6 +441,8 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
   bf16x8 ka[2][4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) ka[0][m] = load_kt(0, m);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) ka[1][m] = load_kt(1, m);
   const float egL = gt[gEg + 63];
   GDN_FENCE();
   // e. Vn as operand slots, plain and scaled by e^(gamma_L - gamma_r)
@@ -480,25 +473,30 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
   OT[1] = mma32(Vnb[2], pf[4], OT[1]);
   OT[1] = mma32(Vnb[3], pf[5], OT[1]);
   GDN_FENCE();
-  // g. S' = e^gamma_L S + K^T (dec Vn), k-step by k-step, the next k-step's
-  //    K^T slots read while the current one's products run
+  // g. S' = e^gamma_L S + K^T (dec Vn), k-step by k-step, the K^T slots read
+  //    two k-steps ahead; h. the output slice, scaled, into the v rows (own
+  //    columns only: this wave has read them already; lane = row r, 4
+  //    consecutive columns), placed between g's products so that its VALU
+  //    and LDS work overlaps them
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[m][i] *= egL;
+  bf16x8 kb3[4];
+  auto g_step = [&](const bf16x8(&kf)[4], int st) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s + 1 < 4) {
+    for (int m = 0; m < 4; ++m) S[m] = mma32(kf[m], Vnd[st], S[m]);
+  };
 #pragma unroll
-      for (int m = 0; m < 4; ++m) ka[(s + 1) & 1][m] = load_kt(s + 1, m);
-    }
-    GDN_FENCE();
+  for (int m = 0; m < 4; ++m) kb3[m] = load_kt(2, m);
+  GDN_FENCE();
+  g_step(ka[0], 0);
+  GDN_FENCE();
 #pragma unroll
-    for (int m = 0; m < 4; ++m) S[m] = mma32(ka[s & 1][m], Vnd[s], S[m]);
-    GDN_FENCE();
-  }
-  // h. the output slice, scaled, into the v rows (own columns only: this
-  //    wave has read them already): lane = row r, 4 consecutive columns
+  for (int m = 0; m < 4; ++m) ka[0][m] = load_kt(3, m);
+  GDN_FENCE();
+  g_step(ka[1], 1);
+  GDN_FENCE();
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     bf16 *orow = sV + (32 * t + r32) * PITCH + 32 * j + 4 * h;
@@ -507,6 +505,10 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
       st4(orow + 8 * b, OT[t][4 * b] * scale, OT[t][4 * b + 1] * scale,
           OT[t][4 * b + 2] * scale, OT[t][4 * b + 3] * scale);
   }
+  GDN_FENCE();
+  g_step(kb3, 2);
+  GDN_FENCE();
+  g_step(ka[0], 3);
 }
 #undef GDN_FENCE
 

@@ -40,7 +40,7 @@ struct FwdWorkspace {
 
 struct BwdWorkspace {
   FwdWorkspace fwd;  // forward state recompute (its own pieces)
-  size_t hstates = 0;   // element type [NC][Hv][V][K]: state entering each chunk, transposed
+  size_t hstates = 0;   // element type [NC][Hv][K*V]: state entering each chunk, lane layout (gdn_seg.hpp)
   size_t dstates = 0;   // element type [NC][Hv][V][K]: gradient of the state leaving each chunk, transposed
   size_t dseg = 0;      // fp32 [NS][Hv][K][V]: reverse segment partials
   size_t deseg = 0;     // fp32 [NS][Hv][K][V]
@@ -78,7 +78,7 @@ struct BwdArgs {
   // set with in-library q/k L2 normalisation (q, k then point at the
   // normalised rows): per-row factors for the chain rule of dq, dk
   const float *rq = nullptr, *rk = nullptr;
-  // the forward's state cache ([chunks][Hv][V][K], element type), or null:
+  // the forward's state cache ([chunks][Hv][K*V], element type, lane layout), or null:
   // then the states are recomputed into the workspace
   const void *hcache = nullptr;
   const void *tm_ext = nullptr;  // per-chunk T of the same cache

@@ -360,6 +360,90 @@ __device__ __forceinline__ void mirror_store_t(const E *srcT, E *dstT, int tid =
   }
 }
 
+// ---- per-chunk states in the "lane layout" (state cache, backward's states)
+// The forward's register-resident pass keeps S in 32x32 MFMA accumulators
+// (gdn_fwd_slice.hip); the state cache stores S as those registers hold it,
+// so that pass writes it as whole 1 KB pieces: element (k, v) of S sits at
+//   ((v / 32 * (K / 16) + k / 16) * 64 + (v % 32) + 32 h) * 8 + e,
+//   h = (k >> 2) & 1,  e = (k & 3) + 4 ((k >> 3) & 1).
+// Four consecutive k from a multiple of 4 are four consecutive elements, and
+// the 32 columns v0 .. v0 + 31 (v0 % 32 == 0) fill the contiguous range
+// [v0 K, (v0 + 32) K), like 32 rows of S^T.
+template <int K>
+__device__ __forceinline__ uint32_t lane_off(int k, int v) {
+  const int h = (k >> 2) & 1, e = (k & 3) + 4 * ((k >> 3) & 1);
+  return (uint32_t)((((v >> 5) * (K / 16) + (k >> 4)) * 64 + (v & 31) + 32 * h) * 8 + e);
+}
+// The inverse for one 8-element unit u of the layout: its column v and the
+// first k of its two 4-element groups (elements 0..3 and 4..7).
+template <int K>
+__device__ __forceinline__ void lane_unit(int u, int &v, int &k_lo, int &k_hi) {
+  const int lane = u & 63, s = (u >> 6) % (K / 16), j = (u >> 6) / (K / 16);
+  v = 32 * j + (lane & 31);
+  k_lo = 16 * s + 4 * (lane >> 5);
+  k_hi = k_lo + 8;
+}
+
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_old_l(TilesOld<E, K, V> &o, const E *dst,
+                                            int tid = threadIdx.x) {
+  using G = Geo<E, K, V>;
+  const int w = wave_of(tid), lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  if (!G::owns(w)) return;
+  const int rt = G::srt(w);
+#pragma unroll
+  for (int m = 0; m < G::NTS; ++m) {
+    const int ct = G::sct(w) + m;
+    o.x[m] = *reinterpret_cast<const typename E4<E>::type *>(
+        dst + lane_off<K>(16 * rt + 4 * lg, 16 * ct + lr));
+  }
+}
+
+template <typename E, int K, int V>
+__device__ __forceinline__ void tiles_accumulate_l(const Tiles<Geo<E, K, V>::NTS> &s,
+                                                   const TilesOld<E, K, V> &o, E *dst,
+                                                   int tid = threadIdx.x) {
+  using G = Geo<E, K, V>;
+  const int w = wave_of(tid), lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  if (!G::owns(w)) return;
+  const int rt = G::srt(w);
+#pragma unroll
+  for (int m = 0; m < G::NTS; ++m) {
+    const int ct = G::sct(w) + m;
+    E *d = dst + lane_off<K>(16 * rt + 4 * lg, 16 * ct + lr);
+    st4(d, s[m][0] + to_f32(o.x[m][0]), s[m][1] + to_f32(o.x[m][1]),
+        s[m][2] + to_f32(o.x[m][2]), s[m][3] + to_f32(o.x[m][3]));
+  }
+}
+
+// dst (lane layout) = the transposed LDS mirror srcT ([V][G::LDK]); the
+// stores are whole 16-byte pieces in address order.
+template <typename E, int K, int V>
+__device__ __forceinline__ void mirror_store_l(const E *srcT, E *dst, int tid = threadIdx.x) {
+  using G = Geo<E, K, V>;
+  constexpr int NPC = K * V / G::VEC;  // 16-byte pieces
+  constexpr int NP = (NPC + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int m = 0; m < NP; ++m) {
+    const int idx = tid + kThreads * m;
+    if (idx < NPC) {
+      int v, k_lo, k_hi;
+      if (sizeof(E) == 2) {
+        lane_unit<K>(idx, v, k_lo, k_hi);
+        const uint2 a = *reinterpret_cast<const uint2 *>(srcT + v * G::LDK + k_lo);
+        const uint2 b = *reinterpret_cast<const uint2 *>(srcT + v * G::LDK + k_hi);
+        *reinterpret_cast<uint4 *>(dst + idx * G::VEC) = make_uint4(a.x, a.y, b.x, b.y);
+      } else {
+        lane_unit<K>(idx >> 1, v, k_lo, k_hi);
+        *reinterpret_cast<uint4 *>(dst + idx * G::VEC) =
+            *reinterpret_cast<const uint4 *>(srcT + v * G::LDK + ((idx & 1) ? k_hi : k_lo));
+      }
+    }
+  }
+}
+
 // dst[0 .. K V) = src[0 .. K V), or zeros when src is null (fp32 states;
 // kThreads threads).  Every load is in flight before the first store: 16
 // bytes a lane when both pointers allow it, else 4.

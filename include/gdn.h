@@ -105,10 +105,11 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p);
 /* Bytes of the state cache of this problem (0 if invalid).  The cache is an
  * opaque hand-over from gdn_chunk_fwd to gdn_chunk_bwd, the memory-for-
  * compute trade of training: it holds the state entering every chunk (in the
- * element type, transposed, [chunks][Hv][V][K], chunks in token order) and
- * every chunk's T = (I + A)^-1 (element type, [chunks][Hv][64][64], at the
- * next 256-byte boundary).  With it the backward neither recomputes those
- * states nor rebuilds T, and ignores its A argument. */
+ * element type, K * V elements per chunk and v-head, [chunks][Hv] in token
+ * order, each state in the library's internal element order) and every
+ * chunk's T = (I + A)^-1 (element type, [chunks][Hv][64][64], at the next
+ * 256-byte boundary).  With it the backward neither recomputes those states
+ * nor rebuilds T, and ignores its A argument. */
 size_t gdn_state_cache_size(const gdn_problem_t *p);
 
 /* Forward (chunk_gated_delta_rule_fwd of the FlashQLA article, "底层 API").

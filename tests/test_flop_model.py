@@ -61,3 +61,22 @@ def test_backward_model_equals_the_chunked_forms_products(K, V):
     total = _count(chunked.chunk_backward_one, q, k, v, g, beta, 0.5, S0, do, dST, N)
     _, bwd = bench.chunk_flops(K, V)
     assert total - replay + N ** 3 / 3 == bwd
+
+
+def test_kernel_split_of_the_forward_and_min_bytes():
+    """The per-kernel FLOPs of the forward's two kernels add up to the
+    forward's chunked-algorithm count, and the minimum bytes of the headline
+    forward are the inputs read once plus o and the final state (410 MB)."""
+    import synth
+    w = synth.WORKLOADS["hv64_t8192"]
+    nch = 128
+    fwd, _ = bench.chunk_flops(w.K, w.V)
+    split = bench.kernel_flops("prep", w, nch) + bench.kernel_flops("fwd_main", w, nch)
+    assert abs(split - fwd * nch * w.Hv) < 1e-6 * split
+    assert bench.kernel_flops("fwd_fix", w, nch) is None
+    mb = bench.min_bytes(w, 8192, 1, "fwd", 2)
+    assert abs(mb - 409.8e6) < 0.5e6
+    # the backward adds do and dht to the reads, every gradient to the writes
+    # and, in the pages' dataflow, the saved A (fp32, 64 per token and v-head)
+    with_a = bench.min_bytes(w, 8192, 1, "bwd", 2, with_A=True)
+    assert with_a - bench.min_bytes(w, 8192, 1, "bwd", 2) == 8192 * 64 * 64 * 4
