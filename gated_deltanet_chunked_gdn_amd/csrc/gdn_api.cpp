@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cstdint>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -287,6 +288,45 @@ KernelTimer::~KernelTimer() {
 
 }  // namespace gdn
 
+// ---- fixed device scratch of gdn_chunk_fwd_noalloc
+// The workspace of the forward for callers that cannot allocate: one array
+// per device, allocated with the code object and held until the process
+// ends.  Every call on a device uses the same array; nothing in it has to
+// start at zero (each piece a kernel reads is written earlier in the same
+// call), and calls that overlap on one device race on it.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (the host-side name of the array is not a device address).
+int scratch_of_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_ERR_UNSUPPORTED, "device %d beyond the %d devices the scratch table holds",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int gdn_timing_enable(int on) {
@@ -363,26 +403,32 @@ int64_t gdn_plan_segments(const gdn_problem_t *p) {
   return pl.total_segs;
 }
 
-int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
-                  const float *g, const void *beta, const float *h0, void *o, float *ht,
-                  float *g_cum, float *A, float *h, void *state_cache, void *workspace,
-                  size_t ws_bytes, void *stream) {
-  g_err.clear();
-  gdn::Plan pl;
-  int rc = validate(p, &pl);
+}  // extern "C"
+
+namespace {
+
+// Checks of the forward's arguments other than the workspace (no HIP call).
+int fwd_check(const gdn_problem_t *p, gdn::Plan *pl, const void *q, const void *k,
+              const void *v, const float *g, const void *beta, const float *h0, const void *o,
+              const float *ht, const float *g_cum, const float *A, const float *h,
+              const void *state_cache) {
+  int rc = validate(p, pl);
   if (rc != GDN_OK) return rc;
-  if (pl.total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+  if (pl->total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
     return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(g, 4) || !aligned(h0, 4) || !aligned(ht, 4) || !aligned(A, 16) ||
       !aligned(h, 4) || !aligned(g_cum, 4) || !aligned(state_cache, 16))
     return fail(GDN_ERR_LAYOUT,
                 "q, k, v, o, A, state_cache must be 16-byte aligned; fp32 buffers 4-byte");
-  const gdn::FwdWorkspace wl = fwd_layout(p, pl, 0);
-  if (!workspace || ws_bytes < wl.total)
-    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
-                workspace ? ws_bytes : (size_t)0);
-  if (!aligned(workspace, 256)) return fail(GDN_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  return GDN_OK;
+}
+
+// The forward's launches on a checked problem and a large enough workspace.
+int fwd_run(const gdn_problem_t *p, const gdn::Plan &pl, const gdn::FwdWorkspace &wl,
+            const void *q, const void *k, const void *v, const float *g, const void *beta,
+            const float *h0, void *o, float *ht, float *g_cum, float *A, float *h,
+            void *state_cache, void *workspace, void *stream) {
   gdn::FwdArgs a;
   a.p = to_problem(p);
   a.plan = pl;
@@ -415,6 +461,27 @@ int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   if (e != hipSuccess)
     return fail(GDN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_chunk_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
+                  const float *g, const void *beta, const float *h0, void *o, float *ht,
+                  float *g_cum, float *A, float *h, void *state_cache, void *workspace,
+                  size_t ws_bytes, void *stream) {
+  g_err.clear();
+  gdn::Plan pl;
+  int rc = fwd_check(p, &pl, q, k, v, g, beta, h0, o, ht, g_cum, A, h, state_cache);
+  if (rc != GDN_OK) return rc;
+  const gdn::FwdWorkspace wl = fwd_layout(p, pl, 0);
+  if (!workspace || ws_bytes < wl.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  return fwd_run(p, pl, wl, q, k, v, g, beta, h0, o, ht, g_cum, A, h, state_cache, workspace,
+                 stream);
 }
 
 int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
@@ -479,6 +546,28 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   if (e != hipSuccess)
     return fail(GDN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return GDN_OK;
+}
+
+size_t gdn_chunk_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int gdn_chunk_fwd_noalloc(const gdn_problem_t *p, const void *q, const void *k, const void *v,
+                          const float *g, const void *beta, const float *h0, void *o,
+                          float *ht, float *g_cum, float *A, float *h, void *state_cache,
+                          void *stream) {
+  g_err.clear();
+  gdn::Plan pl;
+  int rc = fwd_check(p, &pl, q, k, v, g, beta, h0, o, ht, g_cum, A, h, state_cache);
+  if (rc != GDN_OK) return rc;
+  const gdn::FwdWorkspace wl = fwd_layout(p, pl, 0);
+  if (wl.total > kScratchBytes)
+    return fail(GDN_ERR_WORKSPACE,
+                "problem needs %zu bytes of scratch; the fixed scratch of "
+                "gdn_chunk_fwd_noalloc holds %zu (use gdn_chunk_fwd with a workspace)",
+                wl.total, kScratchBytes);
+  void *ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != GDN_OK) return rc;
+  return fwd_run(p, pl, wl, q, k, v, g, beta, h0, o, ht, g_cum, A, h, state_cache, ws, stream);
 }
 
 int gdn_selftest(void) {

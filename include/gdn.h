@@ -138,6 +138,24 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k,
                   float *dg, float *dh0, const void *state_cache,
                   void *workspace, size_t ws_bytes, void *stream);
 
+/* gdn_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Its scratch is a fixed device array of
+ * gdn_chunk_fwd_noalloc_max_bytes() bytes (128 MiB) inside the library, one
+ * per device, allocated with the library's code object and held until the
+ * process ends; the call itself allocates nothing.  Arguments, layouts and
+ * results are those of gdn_chunk_fwd.  A problem whose workspace
+ * (gdn_chunk_fwd_workspace_size) exceeds the fixed size is rejected with
+ * GDN_ERR_WORKSPACE before anything is enqueued.  Every call on one device
+ * shares that device's array: calls that may overlap on one device (other
+ * streams, other threads) race and must be serialised by the caller. */
+int gdn_chunk_fwd_noalloc(const gdn_problem_t *p, const void *q,
+                          const void *k, const void *v, const float *g,
+                          const void *beta, const float *h0, void *o,
+                          float *ht, float *g_cum, float *A, float *h,
+                          void *state_cache, void *stream);
+size_t gdn_chunk_fwd_noalloc_max_bytes(void);
+
 /* Number of context-parallel segments the forward would launch for this
  * problem (host-only planning query; 0 if invalid). */
 int64_t gdn_plan_segments(const gdn_problem_t *p);

@@ -153,3 +153,22 @@ def test_state_cache_size():
 def test_empty_problem_is_valid():
     p = prob(T=0)
     assert ws(p) > 0
+
+
+def test_noalloc_rejects_oversized_problems_before_any_device_call():
+    """The fixed-scratch forward checks the problem's workspace against its
+    array's size on the host, before it looks the array up on a device."""
+    L = gdn.lib()
+    L.gdn_chunk_fwd_noalloc_max_bytes.restype = ctypes.c_size_t
+    cap = L.gdn_chunk_fwd_noalloc_max_bytes()
+    assert cap == 128 << 20
+    big = prob(T=1 << 20, Hq=8, Hv=16)
+    assert ws(big) > cap
+    assert ws(prob(T=8192, Hq=32, Hv=64)) <= cap  # the headline forward fits
+    P = ctypes.c_void_p
+    rc = L.gdn_chunk_fwd_noalloc(ctypes.byref(big), *([P(256)] * 6), P(256), None, None, None,
+                                 None, None, None)
+    assert rc == 4 and "scratch" in gdn.last_error()
+    rc = L.gdn_chunk_fwd_noalloc(ctypes.byref(prob(Hq=3)), *([P(256)] * 6), P(256), None, None,
+                                 None, None, None, None)
+    assert rc == 2
