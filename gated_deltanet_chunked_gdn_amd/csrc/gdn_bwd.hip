@@ -23,6 +23,8 @@
 // until it is zero or denormal in every element), (3) a chunk-parallel kernel for the local
 // gradients, one workgroup per (chunk, q/k head) summing its v-heads' dq and
 // dk in a fixed order (no atomics).
+#include <stdlib.h>
+
 #include "gdn_seg.hpp"
 
 namespace gdn {
@@ -155,15 +157,15 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
   for (int c = c_end - 1; c >= c_begin && !zero_exit; --c) {
     const int tid = opaque_tid(), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
-    // per-chunk gradients (transposed): pass 1 stores the LDS mirror written
+    // per-chunk gradients (lane layout): pass 1 stores the LDS mirror written
     // last step; the fix-up pass adds its correction, reading the stored
     // values here and writing the sums after phase A
     E *ds = dstates + ((chunk_gid0 + c) * p.Hv + h) * (int64_t)K * V;
     TilesOld<E, K, V> dold;
     if (MODE == kRFix)
-      tiles_old_t<E, K, V>(dold, ds, tid);
+      tiles_old_l<E, K, V>(dold, ds, tid);
     else
-      mirror_store_t<E, K, V>(sDt, ds, tid);
+      mirror_store_l<E, K, V>(sDt, ds, tid);
     // the previous chunk's inputs travel while this whole chunk is computed
     if (c - 1 >= c_begin) {
       const int c1 = c - 1;
@@ -206,7 +208,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
         }
       }
     }
-    if (MODE == kRFix) tiles_accumulate_t<E, K, V>(st, dold, ds, tid);
+    if (MODE == kRFix) tiles_accumulate_l<E, K, V>(st, dold, ds, tid);
     if (MAIN) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -623,27 +625,18 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
     const int h = x.hq * Gq + hl;
     const int64_t cg = x.gid * p.Hv + h;
     const int v0 = vb * VB;
-    // columns v0 .. v0 + VB - 1 of the states: one contiguous block of the
-    // lane layout (S) and rows v0 .. of the transposed gradients (D); each
-    // piece of D is gathered to hold the same elements as its piece of S
+    // columns v0 .. v0 + VB - 1 of the states and of their gradients: one
+    // contiguous block of the lane layout each
     const char *hsb = reinterpret_cast<const char *>(hst + cg * (int64_t)K * V + v0 * K);
-    const E *dsb = dst + cg * (int64_t)K * V + v0 * K;
+    const char *dsb = reinterpret_cast<const char *>(dst + cg * (int64_t)K * V + v0 * K);
 #pragma unroll
     for (int m = 0; m < LP::NSP; ++m) {
       const int idx = tid + kThreads * m;
       uint4 zs = make_uint4(0u, 0u, 0u, 0u), zd = zs;
       if (idx < VB * LP::PK) {
-        zs = *reinterpret_cast<const uint4 *>(hsb + (uint32_t)idx * 16u);
-        int r, k_lo, k_hi;
-        if (sizeof(E) == 2) {
-          lane_unit<K>(idx, r, k_lo, k_hi);
-          const uint2 a = *reinterpret_cast<const uint2 *>(dsb + r * K + k_lo);
-          const uint2 b = *reinterpret_cast<const uint2 *>(dsb + r * K + k_hi);
-          zd = make_uint4(a.x, a.y, b.x, b.y);
-        } else {
-          lane_unit<K>(idx >> 1, r, k_lo, k_hi);
-          zd = *reinterpret_cast<const uint4 *>(dsb + r * K + ((idx & 1) ? k_hi : k_lo));
-        }
+        const uint32_t off = (uint32_t)idx * 16u;
+        zs = *reinterpret_cast<const uint4 *>(hsb + off);
+        zd = *reinterpret_cast<const uint4 *>(dsb + off);
       }
       pf.s[m] = zs;
       pf.d[m] = zd;
@@ -1211,6 +1204,16 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
+// GDN_REV_SLICE=0 in the environment runs reverse pass 1 on the general
+// segment kernel even where the register-resident one applies (comparisons).
+static bool rev_slice_disabled() {
+  static const bool off = [] {
+    const char *e = getenv("GDN_REV_SLICE");
+    return e && e[0] == '0';
+  }();
+  return off;
+}
+
 template <typename E, int K, int V>
 static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   const Problem &p = a.p;
@@ -1241,7 +1244,10 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (pl.total_chunks > 0) {
-    {
+    if (rev_slice_supported(a) && !rev_slice_disabled()) {
+      e = launch_rev_slice_main(a, st);
+      if (e != hipSuccess) return e;
+    } else {
       KernelTimer kt("rev_main", st);
       rev_segment_kernel<E, K, V, kRMain>
           <<<dim3((unsigned)(pl.total_segs * p.Hv)), kThreads, 0, st>>>(a);

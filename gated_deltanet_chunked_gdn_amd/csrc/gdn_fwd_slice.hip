@@ -34,17 +34,10 @@
 //
 // One workgroup barrier per chunk: chain waves read buffer set c & 1 while
 // the helpers fill set (c + 1) & 1, from registers loaded one chunk earlier.
-#include "gdn_seg.hpp"
+#include "gdn_slice.hpp"
 
 namespace gdn {
 namespace slice {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int K = 128, V = 128;
-constexpr int kWaves = 8, kThreadsS = 64 * kWaves;
-constexpr int PITCH = K + 16;  // elements per LDS row of q, k, v (288 bytes: conflict-free 16-byte reads)
-constexpr int PITCH_C = 64 + 16;  // elements per LDS row of T and P (160 bytes)
 
 // One buffer set (element offsets), and the gates (float offsets after it).
 constexpr int oQ = 0, oK = oQ + 64 * PITCH, oV = oK + 64 * PITCH, oT = oV + 64 * PITCH,
@@ -56,39 +49,6 @@ constexpr int SET_BYTES = SET_ELEMS * 2;
 constexpr int LDS_BYTES = 2 * SET_BYTES + 2 * GATE_FLOATS * 4 + 3 * 64 * 4;
 static_assert(SET_BYTES % 16 == 0, "sets stay 16-byte aligned");
 static_assert(LDS_BYTES <= 160 * 1024, "two buffer sets fit the LDS of a compute unit");
-
-__device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 zero16() {
-  f32x16 z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = 0.f;
-  return z;
-}
-// 4-element group q of a 16-element block -> its position group in the pi layout
-__device__ __forceinline__ int pi4(int q) { return (q == 1 || q == 2) ? 3 - q : q; }
-
-__device__ __forceinline__ bf16x8 lds16(const bf16 *p) {
-  return *reinterpret_cast<const bf16x8 *>(p);
-}
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-__device__ __forceinline__ bf16x4 tr4(const bf16 *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
-}
-
-// Operand slots 8 s .. 8 s + 7 of accumulator tile x, rounded to bf16.
-__device__ __forceinline__ bf16x8 slots(const f32x16 &x, int s) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[8 * s + e];
-  return r;
-}
-
-struct Item {
-  SegLoc sl;
-  int h, hq;
-};
 
 // ------------------------------------------------------------------ helpers
 // Helper wave roles (HW = wave - 4):
@@ -119,14 +79,6 @@ struct HelperRegs {
 __device__ __forceinline__ constexpr int q_half(int hw) { return hw == 0 ? 0 : 1; }
 __device__ __forceinline__ constexpr int k_half(int hw) { return hw == 2 ? 1 : 0; }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(x[0], x[1], x[2], x[3]);
-}
 
 // Loads chunk c of the item into the registers of helper role HW.
 template <int HW>
@@ -175,13 +127,6 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const FwdArgs &a,
   R.b = (float)__builtin_bit_cast(bf16, braw);
 }
 
-// A 16-byte piece holding columns 8 pc .. 8 pc + 7 of a row, written into a
-// pi-layout row: its two 4-column groups go to their swapped positions.
-__device__ __forceinline__ void put_pi(bf16 *row, int pc, const uint4 &x) {
-  const int blk = (8 * pc) & ~15, q0 = 2 * (pc & 1);
-  *reinterpret_cast<uint2 *>(row + blk + 4 * pi4(q0)) = make_uint2(x.x, x.y);
-  *reinterpret_cast<uint2 *>(row + blk + 4 * pi4(q0 + 1)) = make_uint2(x.z, x.w);
-}
 
 // Writes the chunk held in R into buffer set `set` (role HW's share).
 template <int HW>
@@ -228,8 +173,7 @@ __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         pv[u] = (j0 + u <= r) ? acc[4 * b + u] * __builtin_amdgcn_exp2f(gr - gj[u]) : 0.f;
-      const int pos = (j0 & ~15) + 4 * pi4((j0 >> 2) & 3);
-      st4(prow + pos, pv[0], pv[1], pv[2], pv[3]);
+      st4(prow + pi_pos(j0), pv[0], pv[1], pv[2], pv[3]);
     }
   } else {
     // v rows (natural layout)
@@ -316,9 +260,6 @@ __device__ __forceinline__ void helper_loop(const FwdArgs &a, const Item &it, ch
 }
 
 // ------------------------------------------------------------- chain waves
-struct ChainCtx {
-  int j, lane, h, r32;
-};
 
 // One chunk of chain wave j on buffer set `set` (gates `gt`): S (4 tiles,
 // rows 32 m .. of K, columns 32 j .. of V) advances by one chunk and the
@@ -336,7 +277,6 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
   const int lane = x.lane, h = x.h, r32 = x.r32, j = x.j;
   const bf16 *sQ = set + oQ, *sK = set + oK, *sT = set + oT, *sP = set + oP;
   bf16 *sV = set + oV;
-  const int G = lane >> 4, sgm = lane & 15;
   // b. K S (rows r, columns of the slice) and O^T = S^T Q^T (rows of the
   //    slice, columns r), over the 8 k-steps of the key dimension; the
   //    state's operand slots (k-step s: rows 16 s .. of S) are rounded to
@@ -357,14 +297,9 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
   for (int s = 0; s < 8; ++s) {
     if (s + 2 < 8) load_b(s + 2, F[(s + 2) % 3]);
     if (s == 5) {
-      // phase c's V at the accumulator positions (transpose reads, 16-lane
-      // group: 4 rows, 16 columns)
-      const int vcol = 32 * j + 16 * (G & 1) + 4 * (sgm & 3);
+      // phase c's V at the accumulator positions
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          vx[t][b] = tr4(sV + (32 * t + 8 * b + 4 * h + (sgm >> 2)) * PITCH + vcol);
+      for (int t = 0; t < 2; ++t) acc_rows(vx[t], sV, t, j, lane);
     }
     GDN_FENCE();
     const bf16x8 sb = slots(S[s >> 1], s & 1);
@@ -429,15 +364,9 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
   Vn[1] = mma32(tf[4], Rb[2], Vn[1]);
   Vn[1] = mma32(tf[5], Rb[3], Vn[1]);
   GDN_FENCE();
-  // g's first operands: K^T slots from transpose reads of the pi-layout k
-  // rows (source lane 4 e + q of a 16-lane group points at row e of the
-  // 4-row block and at the position of column group q)
-  const bf16 *kt_base = sK + (4 * h + (sgm >> 2)) * PITCH + 16 * (G & 1) + 4 * pi4(sgm & 3);
-  auto load_kt = [&](int s, int m) {
-    const bf16 *b = kt_base + 16 * s * PITCH + 32 * m;
-    const bf16x4 lo = tr4(b), hi = tr4(b + 8 * PITCH);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
+  // g's first operands: K^T slots from transpose reads of the pi-layout k rows
+  const TrA kt(sK, PITCH, lane);
+  auto load_kt = [&](int s, int m) { return kt.at(s, m, PITCH); };
   bf16x8 ka[2][4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) ka[0][m] = load_kt(0, m);
@@ -511,27 +440,6 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
   g_step(ka[0], 3);
 }
 #undef GDN_FENCE
-
-// S tiles <-> fp32 [K][V] matrix (row k, column v): lane holds column
-// 32 j + r32 and rows 32 m + 8 (i >> 2) + 4 h + (i & 3).
-__device__ __forceinline__ void state_load(f32x16 (&S)[4], const float *src, const ChainCtx &x) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = 32 * m + 8 * (i >> 2) + 4 * x.h + (i & 3);
-      S[m][i] = src ? src[k * V + 32 * x.j + x.r32] : 0.f;
-    }
-}
-__device__ __forceinline__ void state_store(const f32x16 (&S)[4], float *dst, const ChainCtx &x) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = 32 * m + 8 * (i >> 2) + 4 * x.h + (i & 3);
-      dst[k * V + 32 * x.j + x.r32] = S[m][i];
-    }
-}
 
 __global__ __launch_bounds__(kThreadsS) void slice_main_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];

@@ -41,7 +41,7 @@ struct FwdWorkspace {
 struct BwdWorkspace {
   FwdWorkspace fwd;  // forward state recompute (its own pieces)
   size_t hstates = 0;   // element type [NC][Hv][K*V]: state entering each chunk, lane layout (gdn_seg.hpp)
-  size_t dstates = 0;   // element type [NC][Hv][V][K]: gradient of the state leaving each chunk, transposed
+  size_t dstates = 0;   // element type [NC][Hv][K*V]: gradient of the state leaving each chunk, lane layout
   size_t dseg = 0;      // fp32 [NS][Hv][K][V]: reverse segment partials
   size_t deseg = 0;     // fp32 [NS][Hv][K][V]
   size_t dflags = 0;    // int32 [NS][Hv]
@@ -95,6 +95,10 @@ hipError_t launch_fwd_slice_main(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd_prep(const FwdArgs &a, const float *Ain, hipStream_t stream);
 hipError_t launch_fwd_states(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+// reverse pass 1 of the backward with the gradient in registers
+// (gdn_rev_slice.hip): bf16, K = V = 128
+bool rev_slice_supported(const BwdArgs &a);
+hipError_t launch_rev_slice_main(const BwdArgs &a, hipStream_t stream);
 // q_hat, k_hat (element type) and their per-row factors from raw q, k
 hipError_t launch_l2norm(const Problem &p, int64_t tokens, const void *q, const void *k,
                          void *qn, void *kn, float *rq, float *rk, hipStream_t stream);
