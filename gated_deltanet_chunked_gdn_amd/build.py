@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgdn.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["gdn_api.cpp", "gdn_fwd.hip", "gdn_fwd_slice.hip", "gdn_bwd.hip", "gdn_rev_slice.hip", "gdn_selftest.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_fwd.hip", "gdn_fwd_slice.hip", "gdn_bwd.hip", "gdn_rev_slice.hip", "gdn_grad_slice.hip", "gdn_selftest.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]

@@ -1214,6 +1214,16 @@ static bool rev_slice_disabled() {
   return off;
 }
 
+// GDN_GRAD_SLICE=0 runs the local gradients on local_grad_kernel where the
+// 32x32-tile kernel applies (comparisons).
+static bool grad_slice_disabled() {
+  static const bool off = [] {
+    const char *e = getenv("GDN_GRAD_SLICE");
+    return e && e[0] == '0';
+  }();
+  return off;
+}
+
 template <typename E, int K, int V>
 static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   const Problem &p = a.p;
@@ -1262,7 +1272,10 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     KernelTimer kt("rev_serial", st);
     rev_serial_kernel<E, K, V><<<dim3((unsigned)(p.N * p.Hv)), kThreads, 0, st>>>(a);
   }
-  if (pl.total_chunks > 0) {
+  if (pl.total_chunks > 0 && grad_slice_supported(a) && !grad_slice_disabled()) {
+    e = launch_grad_slice(a, st);
+    if (e != hipSuccess) return e;
+  } else if (pl.total_chunks > 0) {
     KernelTimer kt("local_grad", st);
     // persistent: one workgroup per compute unit (its LDS use leaves room
     // for one), each looping over items

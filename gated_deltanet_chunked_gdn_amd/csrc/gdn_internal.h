@@ -99,6 +99,10 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 // (gdn_rev_slice.hip): bf16, K = V = 128
 bool rev_slice_supported(const BwdArgs &a);
 hipError_t launch_rev_slice_main(const BwdArgs &a, hipStream_t stream);
+// local gradients on 32x32 tiles (gdn_grad_slice.hip): bf16, K = V = 128,
+// q and k given normalised
+bool grad_slice_supported(const BwdArgs &a);
+hipError_t launch_grad_slice(const BwdArgs &a, hipStream_t stream);
 // q_hat, k_hat (element type) and their per-row factors from raw q, k
 hipError_t launch_l2norm(const Problem &p, int64_t tokens, const void *q, const void *k,
                          void *qn, void *kn, float *rq, float *rk, hipStream_t stream);
