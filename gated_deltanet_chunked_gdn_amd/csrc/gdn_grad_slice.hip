@@ -63,16 +63,14 @@ constexpr int kThr = slice::kThreadsS;  // 512
 //   T         [64 rows r][64 t]
 //   Pt        [64 rows t][64 s]   P^T
 //   VnT, dRT  [64 rows v of the block][64 r]
-//   PEt, Ut   [64 rows t][64 s]   (dP * E)^T and the strict part of dKK^T,
-//             over S and D once a v-head's blocks are done
+//   PEt, Ut   [64 rows t][64 s]   (dP * E)^T and the strict part of dKK^T
+//             of the previous v-head
 constexpr int B_QK = 64 * P128 * 2;
 constexpr int B_SD = VB * P128 * 2;
 constexpr int B_C = 64 * P64 * 2;
 constexpr int oQ = 0, oK = oQ + B_QK, oS = oK + B_QK, oD = oS + B_SD, oO = oD + B_SD,
               oV = oO + B_C, oT = oV + B_C, oPt = oT + B_C, oVnT = oPt + B_C,
-              oDRT = oVnT + B_C, oF = oDRT + B_C;
-constexpr int oPEt = oS, oUt = oD;
-static_assert(B_C <= B_SD, "aliases");
+              oDRT = oVnT + B_C, oPEt = oDRT + B_C, oUt = oPEt + B_C, oF = oUt + B_C;
 
 // per-row values: gates (two sets, alternating over v-heads) and the partial
 // row and column sums of dbeta and dgamma, each with its own contributor slot
@@ -462,6 +460,80 @@ __device__ __forceinline__ void write_pt(const f32x16 (&raw)[2], const Ctx &c, i
   }
 }
 
+// End of a v-head, dP / dA holders: (dP * E)^T and dKK^T (strict part) of
+// their tiles into LDS, with the row and column sums for dgamma, dbeta.
+template <int ROLE>
+__device__ __forceinline__ void e_tiles_out(const f32x16 (&eacc)[2], const f32x16 (&eraw)[2],
+                                            const Ctx &c, int set, float scale) {
+  using R = Role<ROLE>;
+  Small &sm = c.sm();
+#pragma unroll
+  for (int j = 0; j < R::NE; ++j) {
+    const int pt = R::E0 + j, st = e_st(pt), tt = e_tt(pt);
+    const int t = 32 * tt + c.r32;
+    const float gt = sm.gam[set][t];
+    float gs[16], bs[16];
+    rows16(gs, sm.gam[set], st, c.h);
+    rows16(bs, sm.bet[set], st, c.h);
+    f32x16 out;
+    float rsum[16], dbk[16], csum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = 32 * st + acc_row(i, c.h);
+      if constexpr (R::kHoldP) {
+        const bool in = t <= s;
+        const float e = in ? __builtin_amdgcn_exp2f(gs[i] - gt) : 0.f;
+        const float pe = in ? scale * eacc[j][i] * e : 0.f;
+        out[i] = pe;
+        rsum[i] = pe * eraw[j][i];
+      } else {
+        const bool in = t < s;
+        const float e = in ? __builtin_amdgcn_exp2f(gs[i] - gt) : 0.f;
+        const float dam = in ? -eacc[j][i] : 0.f;
+        const float kkv = in ? bs[i] * dam * e : 0.f;
+        out[i] = kkv;
+        rsum[i] = kkv * eraw[j][i];
+        dbk[i] = dam * eraw[j][i] * e;
+      }
+      csum += rsum[i];
+    }
+    bf16 *dst = c.bf(R::kHoldP ? oPEt : oUt) + t * P64 + 32 * st + 8 * c.h;
+    *reinterpret_cast<bf16x8 *>(dst) = slots(out, 0);
+    *reinterpret_cast<bf16x8 *>(dst + 16) = slots(out, 1);
+    reduce_rows_to(R::kHoldP ? sm.rsP[pt] : sm.rsA[pt], rsum, c.lane);
+    if constexpr (!R::kHoldP) reduce_rows_to(sm.dbA[pt], dbk, c.lane);
+    csum += __shfl_xor(csum, 32, 64);
+    if (c.h == 0) (R::kHoldP ? sm.csP[pt] : sm.csA[pt])[c.r32] = csum;
+  }
+}
+
+// dq += (dP * E) K;  dk += (dP * E)^T Q + (dKK + dKK^T) K  (dq, dk waves)
+__device__ __forceinline__ void e_products(f32x16 (&dq)[2], f32x16 (&dk)[2], int rt, int kp,
+                                           const Ctx &c) {
+  const TrA trPE(c.bf(oPEt), P64, c.lane), trU(c.bf(oUt), P64, c.lane);
+  const TrA trK(c.bf(oK), P128, c.lane), trQ(c.bf(oQ), P128, c.lane);
+  const bf16 *ppe = c.bf(oPEt) + (32 * rt + c.r32) * P64 + 8 * c.h;
+  const bf16 *pu = c.bf(oUt) + (32 * rt + c.r32) * P64 + 8 * c.h;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 ape = trPE.at(s, rt, P64), apt = lds16(ppe + 16 * s);
+    // dKK^T has its strict part only: the two reads never overlap
+    const uint4 x1 = __builtin_bit_cast(uint4, lds16(pu + 16 * s));
+    const uint4 x2 = __builtin_bit_cast(uint4, trU.at(s, rt, P64));
+    const bf16x8 am = __builtin_bit_cast(
+        bf16x8, make_uint4(x1.x | x2.x, x1.y | x2.y, x1.z | x2.z, x1.w | x2.w));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kt = 2 * kp + j;
+      const bf16x8 kb = trK.at(s, kt, P128);
+      dq[j] = mma32(ape, kb, dq[j]);
+      dk[j] = mma32(apt, trQ.at(s, kt, P128), dk[j]);
+      dk[j] = mma32(am, kb, dk[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int ROLE>
 __device__ void run(const BwdArgs &a, const Ctx &c0) {
   using R = Role<ROLE>;
@@ -535,6 +607,13 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
             load_head(pf, a, x, nhl, any, c);
             load_qk(pf, a, x, !in_item && has_next, c);
           }
+        }
+        if (vb == 0 && hl > 0) {
+          // this v-head's P^T (its gates were committed at the end of the
+          // previous v-head); the previous v-head's dg, dbeta
+          if constexpr (R::kHoldP) write_pt<ROLE>(eraw, c, set);
+          if constexpr (ROLE == 1) store_gates(a, cur, hl - 1, set ^ 1, c);
+          if constexpr (!R::kV) e_products(dq, dk, rt, kp, c);
         }
         __syncthreads();
         // ---------------------------------------------------------- phase V
@@ -732,112 +811,32 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
           }
         }
       }
-      // ------------------------------------------------ end of the v-head
-      c.relane();
-      __syncthreads();  // dP, dA complete; S, D free for (dP * E)^T, dKK^T
+      // ---- end of the v-head (no barrier needed: each wave works on its own
+      // registers; the LDS it writes is not read before the next barrier)
+      // the held dP, dA tiles are complete
       if constexpr (R::kV) {
-#pragma unroll
-        for (int j = 0; j < R::NE; ++j) {
-          const int pt = R::E0 + j, st = e_st(pt), tt = e_tt(pt);
-          const int t = 32 * tt + c.r32;
-          const float gt = sm.gam[set][t];
-          float gs[16], bs[16];
-          rows16(gs, sm.gam[set], st, c.h);
-          rows16(bs, sm.bet[set], st, c.h);
-          f32x16 out;
-          float rsum[16], dbk[16], csum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int s = 32 * st + acc_row(i, c.h);
-            if constexpr (R::kHoldP) {
-              const bool in = t <= s;
-              const float e = in ? __builtin_amdgcn_exp2f(gs[i] - gt) : 0.f;
-              const float pe = in ? scale * eacc[j][i] * e : 0.f;
-              out[i] = pe;
-              rsum[i] = pe * eraw[j][i];
-            } else {
-              const bool in = t < s;
-              const float e = in ? __builtin_amdgcn_exp2f(gs[i] - gt) : 0.f;
-              const float dam = in ? -eacc[j][i] : 0.f;
-              const float kkv = in ? bs[i] * dam * e : 0.f;
-              out[i] = kkv;
-              rsum[i] = kkv * eraw[j][i];
-              dbk[i] = dam * eraw[j][i] * e;
-            }
-            csum += rsum[i];
-          }
-          bf16 *dst = c.bf(R::kHoldP ? oPEt : oUt) + t * P64 + 32 * st + 8 * c.h;
-          *reinterpret_cast<bf16x8 *>(dst) = slots(out, 0);
-          *reinterpret_cast<bf16x8 *>(dst + 16) = slots(out, 1);
-          reduce_rows_to(R::kHoldP ? sm.rsP[pt] : sm.rsA[pt], rsum, c.lane);
-          if constexpr (!R::kHoldP) reduce_rows_to(sm.dbA[pt], dbk, c.lane);
-          csum += __shfl_xor(csum, 32, 64);
-          if (c.h == 0) (R::kHoldP ? sm.csP[pt] : sm.csA[pt])[c.r32] = csum;
-        }
-        if constexpr (ROLE == 3) {
-          // the tile above the diagonal (rows t 32..63, positions 0..31) is 0
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const int q = c.lane + 64 * m;
-            const int off = (32 + (q >> 2)) * P64 + 8 * (q & 3);
-            *reinterpret_cast<uint4 *>(c.bf(oPEt) + off) = make_uint4(0u, 0u, 0u, 0u);
-            *reinterpret_cast<uint4 *>(c.bf(oUt) + off) = make_uint4(0u, 0u, 0u, 0u);
-          }
-        }
+        e_tiles_out<ROLE>(eacc, eraw, c, set, scale);
       } else {
         reduce_rows_to(sm.pq[kp] + 32 * rt, pq, c.lane);
         reduce_rows_to(sm.pc[kp] + 32 * rt, pc, c.lane);
         reduce_rows_to(sm.pa2[kp] + 32 * rt, pa2, c.lane);
       }
-      {
-        const float gsum = wave_sum(glp);
-        if (c.lane == 0) sm.gl[c.w] = gsum;
-        glp = 0.f;
-      }
+      const float gsum = wave_sum(glp);
+      if (c.lane == 0) sm.gl[c.w] = gsum;
+      glp = 0.f;
       if (hl + 1 < Gq) {
+        // the next v-head's T (sT is no longer read) and gates
         commit_head(pf, c);
         if (c.w == 7) commit_gates(pf, c, set ^ 1);
       }
-      __syncthreads();
-      if constexpr (R::kV) {
-        if constexpr (ROLE == 3) store_gates(a, cur, hl, set, c);
-        if constexpr (R::kHoldP) {
-          if (hl + 1 < Gq) write_pt<ROLE>(eraw, c, set ^ 1);
-        }
-      } else {
-        // dq += (dP * E) K;  dk += (dP * E)^T Q + (dKK + dKK^T) K
-        const TrA trPE(c.bf(oPEt), P64, c.lane), trU(c.bf(oUt), P64, c.lane);
-        const TrA trK(c.bf(oK), P128, c.lane), trQ(c.bf(oQ), P128, c.lane);
-        const bf16 *ppe = c.bf(oPEt) + (32 * rt + c.r32) * P64 + 8 * c.h;
-        const bf16 *pu = c.bf(oUt) + (32 * rt + c.r32) * P64 + 8 * c.h;
-        bf16x8 ape[4], apt[4], am[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          ape[s] = trPE.at(s, rt, P64);
-          apt[s] = lds16(ppe + 16 * s);
-          // dKK^T has its strict part only: the two reads never overlap
-          const uint4 x1 = __builtin_bit_cast(uint4, lds16(pu + 16 * s));
-          const uint4 x2 = __builtin_bit_cast(uint4, trU.at(s, rt, P64));
-          am[s] = __builtin_bit_cast(
-              bf16x8, make_uint4(x1.x | x2.x, x1.y | x2.y, x1.z | x2.z, x1.w | x2.w));
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int kt = 2 * kp + j;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 kb = trK.at(s, kt, P128);
-            dq[j] = mma32(ape[s], kb, dq[j]);
-            dk[j] = mma32(apt[s], trQ.at(s, kt, P128), dk[j]);
-            dk[j] = mma32(am[s], kb, dk[j]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
       ++u;
     }
-    // ---- item end: dq, dk of the q/k head out through LDS
+    // ---- item end: the last v-head's chunk-matrix products and gates, then
+    // dq, dk of the q/k head out through LDS
     c.relane();
+    __syncthreads();
+    if constexpr (!R::kV) e_products(dq, dk, rt, kp, c);
+    if constexpr (ROLE == 1) store_gates(a, cur, Gq - 1, (u - 1) & 1, c);
     __syncthreads();
     if constexpr (!R::kV) {
 #pragma unroll
@@ -880,10 +879,13 @@ __global__ __launch_bounds__(kThr) void grad_slice_kernel(BwdArgs a) {
   c.lane = threadIdx.x & 63;
   c.h = c.lane >> 5;
   c.r32 = c.lane & 31;
-  // P^T above the diagonal (rows t 32..63, positions 0..31) is 0 throughout
+  // P^T, (dP * E)^T and dKK^T above the diagonal (rows t 32..63, positions
+// 0..31) are 0 throughout
   if (c.tid < 128) {
     const int off = (32 + (c.tid >> 2)) * P64 + 8 * (c.tid & 3);
     *reinterpret_cast<uint4 *>(c.bf(oPt) + off) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4 *>(c.bf(oPEt) + off) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4 *>(c.bf(oUt) + off) = make_uint4(0u, 0u, 0u, 0u);
   }
   switch (c.w) {
     case 0: run<0>(a, c); break;
