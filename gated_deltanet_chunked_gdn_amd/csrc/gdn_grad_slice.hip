@@ -593,10 +593,13 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
         c.relane();
         __syncthreads();  // the previous block's readers are done
         commit_block(pf, c, glp);
-        {
-          // the block after this one: the next V block, else the next
-          // v-head's first block (with its T and gates: loaded in a v-head's
-          // last block), else the next item's (with its q, k)
+        // the block after this one: the next V block, else the next v-head's
+        // first block (with its T and gates: loaded in a v-head's last
+        // block), else the next item's (with its q, k).  Waves 4..7 issue
+        // their share of the loads at the start of phase V (theirs is the
+        // shorter one), waves 0..3 theirs at its end, so that the two halves
+        // do not queue together.
+        auto prefetch = [&]() {
           const bool in_head = vb + 1 < NVB, in_item = in_head || hl + 1 < Gq;
           const GItem x = pick(in_item, cur, nxt);
           const int nhl = in_head ? hl : (in_item ? hl + 1 : 0);
@@ -607,7 +610,7 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
             load_head(pf, a, x, nhl, any, c);
             load_qk(pf, a, x, !in_item && has_next, c);
           }
-        }
+        };
         if (vb == 0 && hl > 0) {
           // this v-head's P^T (its gates were committed at the end of the
           // previous v-head); the previous v-head's dg, dbeta
@@ -714,6 +717,7 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
             for (int i = 0; i < 16; ++i) pa1[t][i] = dr[t][i] * vv[i];
           }
         } else {
+          prefetch();
           // X = dO S^T for dq tiles (rt, 2 kp + j); row dot with Q
           const bf16 *pa = c.bf(oO) + (32 * rt + c.r32) * P64 + 8 * c.h;
           bf16x8 ao[4];
@@ -738,6 +742,7 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        if constexpr (R::kV) prefetch();
         __syncthreads();
         // ---------------------------------------------------------- phase K
         store_dv(a, cur, hl, vb, set, c);
