@@ -169,8 +169,9 @@ __device__ __forceinline__ const bf16 *states_of(const BwdArgs &a) {
 // where the branches join, which waits for the loads right after their issue.
 //
 // S, D, dO and V of block vb of v-head hl (rows past the chunk read 0)
+// (parts: 1 = S and D, 2 = dO and V, 3 = all)
 __device__ __forceinline__ void load_block(Pref &pf, const BwdArgs &a, const GItem &x, int hl,
-                                           int vb, bool on, const Ctx &c) {
+                                           int vb, bool on, const Ctx &c, int part = 3) {
   const Problem &p = a.p;
   const int h = x.hq * (p.Hv / p.Hq) + hl;
   const int64_t cg = x.gid * p.Hv + h;
@@ -179,12 +180,15 @@ __device__ __forceinline__ void load_block(Pref &pf, const BwdArgs &a, const GIt
   const auto rd = slice::rsrc_of(reinterpret_cast<const bf16 *>(a.ws + a.wl.dstates) +
                                      cg * (K * slice::V),
                                  kv_bytes);
+  if (part & 1) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const uint32_t off = (uint32_t)(vb * 1024 + c.tid + kThr * m) * 16u;
-    pf.s[m] = slice::bload16(rs, off);
-    pf.d[m] = slice::bload16(rd, off);
+    for (int m = 0; m < 2; ++m) {
+      const uint32_t off = (uint32_t)(vb * 1024 + c.tid + kThr * m) * 16u;
+      pf.s[m] = slice::bload16(rs, off);
+      pf.d[m] = slice::bload16(rd, off);
+    }
   }
+  if (!(part & 2)) return;
   const uint32_t v_rs = (uint32_t)(p.Hv * slice::V * 2);
   const int64_t e0 = (x.tok0 * p.Hv + h) * slice::V + vb * VB;
   const uint32_t vbytes = on ? x.rows * v_rs : 0u;
@@ -597,16 +601,16 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
         // first block (with its T and gates: loaded in a v-head's last
         // block), else the next item's (with its q, k).  Waves 4..7 issue
         // their share of the loads at the start of phase V (theirs is the
-        // shorter one), waves 0..3 theirs at its end, so that the two halves
-        // do not queue together.
-        auto prefetch = [&]() {
+        // shorter one), waves 0..3 theirs at its end and at the start of
+        // phase K, so that the loads of the workgroup do not queue together.
+        auto prefetch = [&](int part) {
           const bool in_head = vb + 1 < NVB, in_item = in_head || hl + 1 < Gq;
           const GItem x = pick(in_item, cur, nxt);
           const int nhl = in_head ? hl : (in_item ? hl + 1 : 0);
           const int nvb = in_head ? vb + 1 : 0;
           const bool any = in_item || has_next;
-          load_block(pf, a, x, nhl, nvb, any, c);
-          if (vb + 1 == NVB) {
+          load_block(pf, a, x, nhl, nvb, any, c, part);
+          if ((part & 2) && vb + 1 == NVB) {
             load_head(pf, a, x, nhl, any, c);
             load_qk(pf, a, x, !in_item && has_next, c);
           }
@@ -717,7 +721,7 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
             for (int i = 0; i < 16; ++i) pa1[t][i] = dr[t][i] * vv[i];
           }
         } else {
-          prefetch();
+          prefetch(3);
           // X = dO S^T for dq tiles (rt, 2 kp + j); row dot with Q
           const bf16 *pa = c.bf(oO) + (32 * rt + c.r32) * P64 + 8 * c.h;
           bf16x8 ao[4];
@@ -742,9 +746,10 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        if constexpr (R::kV) prefetch();
+        if constexpr (R::kV) prefetch(2);
         __syncthreads();
         // ---------------------------------------------------------- phase K
+        if constexpr (R::kV) prefetch(1);
         store_dv(a, cur, hl, vb, set, c);
         if constexpr (R::kV) {
           const TrA trVn(c.bf(oVnT), P64, c.lane);
