@@ -220,7 +220,9 @@ __device__ __forceinline__ void helper_step(HelperRegs<HW> &Rc, HelperRegs<HW> &
                                             const FwdArgs &a, const Item &it, int c, char *smem,
                                             float *scratch, int lane) {
   const int c0 = it.sl.c_begin, c1 = it.sl.c_end;
-  helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane);
+  // role 1 has the shortest step: its loads go last, so that the roles whose
+  // commit and P tile the next barrier waits for are not queued behind them
+  if (HW != 1) helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane);
   if (HW == 1) {
     const int cp = max(c - 1, c0);
     const int rows = c > c0 ? min(kChunk, it.sl.si.len - cp * kChunk) : 0;
@@ -230,6 +232,7 @@ __device__ __forceinline__ void helper_step(HelperRegs<HW> &Rc, HelperRegs<HW> &
   helper_commit<HW>(Rc, reinterpret_cast<bf16 *>(smem + (cn & 1) * SET_BYTES),
                     reinterpret_cast<float *>(smem + 2 * SET_BYTES) + (cn & 1) * GATE_FLOATS,
                     scratch, lane);
+  if (HW == 1) helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane);
 }
 
 template <int HW>
