@@ -52,10 +52,10 @@ static_assert(LDS_BYTES <= 160 * 1024, "two buffer sets fit the LDS of a compute
 
 // ------------------------------------------------------------------ helpers
 // Helper wave roles (HW = wave - 4):
-//   0  q, k and T rows 0..31 into LDS; P tile (rows 0..31, columns 0..31)
+//   0  q, k rows 0..31 into LDS; P tile (rows 0..31, columns 0..31)
 //   1  the previous chunk's output rows out of LDS, then v rows into the
-//      same LDS rows (one wave, so the reads come before the writes)
-//   2  q, k and T rows 32..63 into LDS; P tile (rows 32..63, columns 32..63)
+//      same LDS rows (one wave, so the reads come before the writes); T
+//   2  q, k rows 32..63 into LDS; P tile (rows 32..63, columns 32..63)
 //   3  the gates; P tile (rows 32..63, columns 0..31)
 // (P is lower triangular: its tile (rows 0..31, columns 32..63) is zero and
 // never read.)  Rows are loaded whole (16 consecutive lanes cover one
@@ -68,9 +68,9 @@ static_assert(LDS_BYTES <= 160 * 1024, "two buffer sets fit the LDS of a compute
 template <int HW>
 struct HelperRegs {
   // roles 0, 2, 3: q rows (buf[0..7]) and k rows (buf[8..15]) of one half of
-  // the chunk, 16-byte piece lane & 15 of row 4 m + (lane >> 4); roles 0, 2
-  // also 4 pieces of T (buf[16..19]); role 1: v rows (buf[0..15])
-  static constexpr int NB = (HW == 0 || HW == 2) ? 20 : 16;
+  // the chunk, 16-byte piece lane & 15 of row 4 m + (lane >> 4); role 1: v
+  // rows (buf[0..15]) and T (buf[16..23], 16-byte piece lane + 64 m)
+  static constexpr int NB = HW == 1 ? 24 : 16;
   uint4 buf[NB];
   float g;
   float b;
@@ -107,14 +107,14 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const FwdArgs &a,
 #pragma unroll
     for (int m = 0; m < 16; ++m) R.buf[m] = bload16(rv, (uint32_t)(4 * m + r16) * rs + 16u * pc);
   }
-  if (HW == 0 || HW == 2) {
-    // T rows 0..31 (role 0) or 32..63 (role 2): 8 16-byte pieces a row
+  if (HW == 1) {
+    // T (role 1, which has the shortest step): 8 16-byte pieces a row
     const int64_t cgid = it.sl.chunk0 + c;
     const uint4 *tb = reinterpret_cast<const uint4 *>(
         reinterpret_cast<const bf16 *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat) +
         (cgid * p.Hv + it.h) * 64 * 64);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) R.buf[16 + m] = tb[lane + 64 * (m + 2 * HW)];
+    for (int m = 0; m < 8; ++m) R.buf[16 + m] = tb[lane + 64 * m];
   }
   // every role keeps the chunk's gates (P needs gamma); rows past the end: 0
   const uint32_t gs = (uint32_t)(p.Hv * 4);
@@ -144,14 +144,6 @@ __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set
       put_pi(set + oQ + (32 * rbq + 4 * m + r16) * PITCH, pc, R.buf[m]);
       put_pi(set + oK + (32 * rbk + 4 * m + r16) * PITCH, pc, R.buf[8 + m]);
     }
-    if (HW != 3) {
-      // T rows (pi layout)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int idx = lane + 64 * (m + 2 * HW);  // 16-byte piece of T
-        put_pi(set + oT + (idx >> 3) * PITCH_C, idx & 7, R.buf[16 + m]);
-      }
-    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -176,10 +168,15 @@ __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set
       st4(prow + pi_pos(j0), pv[0], pv[1], pv[2], pv[3]);
     }
   } else {
-    // v rows (natural layout)
+    // v rows (natural layout), T rows (pi layout)
 #pragma unroll
     for (int m = 0; m < 16; ++m)
       *reinterpret_cast<uint4 *>(set + oV + (4 * m + r16) * PITCH + 8 * pc) = R.buf[m];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int idx = lane + 64 * m;  // 16-byte piece of T
+      put_pi(set + oT + (idx >> 3) * PITCH_C, idx & 7, R.buf[16 + m]);
+    }
   }
   if (HW == 3) {
     // the gates
