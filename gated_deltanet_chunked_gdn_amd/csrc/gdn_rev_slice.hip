@@ -233,16 +233,14 @@ __device__ __forceinline__ void chain_step(f32x16 (&D)[4], const bf16 *set, cons
     yb[2 * t] = slots(yv, 0);
     yb[2 * t + 1] = slots(yv, 1);
   }
-  // a, b. K D over the key dimension (the leaving gradient's slots, stored
-  //    to the per-chunk gradients as they are formed), and
-  //    D <- e^gamma_L D + Q^T Y interleaved with it
+  // a, b. K D over the key dimension, and D <- e^gamma_L D + Q^T Y
+  //    interleaved with it (the leaving gradient's slots are stored to the
+  //    per-chunk gradients at the end of the step: at its start the helpers'
+  //    loads fill the memory queue, and the stores would wait behind them)
   const float egL = gt[gEg + 63];
   bf16x8 Db[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    Db[s] = slots(D[s >> 1], s & 1);
-    if (dcache) *reinterpret_cast<bf16x8 *>(dcache + ((j * 8 + s) * 64 + lane) * 8) = Db[s];
-  }
+  for (int s = 0; s < 8; ++s) Db[s] = slots(D[s >> 1], s & 1);
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -321,6 +319,11 @@ __device__ __forceinline__ void chain_step(f32x16 (&D)[4], const bf16 *set, cons
 #pragma unroll
     for (int m = 0; m < 4; ++m) D[m] = mma32(ka[m], xb[s], D[m]);
     GDN_FENCE();
+  }
+  if (dcache) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      *reinterpret_cast<bf16x8 *>(dcache + ((j * 8 + s) * 64 + lane) * 8) = Db[s];
   }
 }
 #undef GDN_FENCE
