@@ -293,6 +293,9 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
   load_b(0, F[0]);
   load_b(1, F[1]);
   bf16x4 vx[2][4];
+  // the entering state's slots for the state cache, stored at the end of
+  // the step (at its start the helpers' loads fill the memory queue)
+  bf16x8 Sb[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     if (s + 2 < 8) load_b(s + 2, F[(s + 2) % 3]);
@@ -303,11 +306,7 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
     }
     GDN_FENCE();
     const bf16x8 sb = slots(S[s >> 1], s & 1);
-    if (hcache) {
-      // the lane layout of the state cache is these very slots: one whole
-      // 1 KB piece per k-step and wave
-      *reinterpret_cast<bf16x8 *>(hcache + ((j * 8 + s) * 64 + lane) * 8) = sb;
-    }
+    if (hcache) Sb[s] = sb;
     const bf16x8(&f)[4] = F[s % 3];
     KS[0] = mma32(f[0], sb, KS[0]);
     KS[1] = mma32(f[1], sb, KS[1]);
@@ -438,6 +437,13 @@ __device__ __forceinline__ void chain_step(f32x16 (&S)[4], bf16 *set, const floa
   g_step(kb3, 2);
   GDN_FENCE();
   g_step(ka[0], 3);
+  if (hcache) {
+    // the lane layout of the state cache is these very slots: one whole 1 KB
+    // piece per k-step and wave
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      *reinterpret_cast<bf16x8 *>(hcache + ((j * 8 + s) * 64 + lane) * 8) = Sb[s];
+  }
 }
 #undef GDN_FENCE
 
