@@ -82,8 +82,9 @@ __device__ __forceinline__ constexpr int k_half(int hw) { return hw == 2 ? 1 : 0
 
 // Loads chunk c of the item into the registers of helper role HW.
 template <int HW>
+// (parts: 1 = everything but the k rows, 2 = the k rows, 3 = all)
 __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const FwdArgs &a, const Item &it,
-                                            int c, int lane) {
+                                            int c, int lane, int part = 3) {
   const Problem &p = a.p;
   const int64_t tok0 = it.sl.si.tok0 + (int64_t)c * kChunk;
   const int rows = min(kChunk, it.sl.si.len - c * kChunk);
@@ -97,9 +98,10 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const FwdArgs &a,
     for (int m = 0; m < 8; ++m) {
       const uint32_t rq0 = (uint32_t)(32 * q_half(HW) + 4 * m + r16);
       const uint32_t rk0 = (uint32_t)(32 * k_half(HW) + 4 * m + r16);
-      R.buf[m] = bload16(rq, rq0 * rs + 16u * pc);
-      R.buf[8 + m] = bload16(rk, rk0 * rs + 16u * pc);
+      if (part & 1) R.buf[m] = bload16(rq, rq0 * rs + 16u * pc);
+      if (part & 2) R.buf[8 + m] = bload16(rk, rk0 * rs + 16u * pc);
     }
+    if (!(part & 1)) return;
   } else {
     const uint32_t rs = (uint32_t)(p.Hv * V * 2);
     const bf16 *vb = reinterpret_cast<const bf16 *>(a.v) + (tok0 * p.Hv + it.h) * V;
@@ -218,8 +220,9 @@ __device__ __forceinline__ void helper_step(HelperRegs<HW> &Rc, HelperRegs<HW> &
                                             float *scratch, int lane) {
   const int c0 = it.sl.c_begin, c1 = it.sl.c_end;
   // role 1 has the shortest step: its loads go last, so that the roles whose
-  // commit and P tile the next barrier waits for are not queued behind them
-  if (HW != 1) helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane);
+  // commit and P tile the next barrier waits for are not queued behind them;
+  // those roles issue their k rows after the commit
+  if (HW != 1) helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane, 1);
   if (HW == 1) {
     const int cp = max(c - 1, c0);
     const int rows = c > c0 ? min(kChunk, it.sl.si.len - cp * kChunk) : 0;
@@ -230,6 +233,7 @@ __device__ __forceinline__ void helper_step(HelperRegs<HW> &Rc, HelperRegs<HW> &
                     reinterpret_cast<float *>(smem + 2 * SET_BYTES) + (cn & 1) * GATE_FLOATS,
                     scratch, lane);
   if (HW == 1) helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane);
+  if (HW != 1) helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane, 2);
 }
 
 template <int HW>
