@@ -57,8 +57,9 @@ __device__ __forceinline__ constexpr int q_half(int hw) { return hw == 0 ? 0 : 1
 __device__ __forceinline__ constexpr int k_half(int hw) { return hw == 2 ? 1 : 0; }
 
 template <int HW>
+// (parts: 1 = everything but the k rows, 2 = the k rows, 3 = all)
 __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const BwdArgs &a, const Item &it,
-                                            int c, int lane) {
+                                            int c, int lane, int part = 3) {
   const Problem &p = a.p;
   const int64_t tok0 = it.sl.si.tok0 + (int64_t)c * kChunk;
   const int rows = min(kChunk, it.sl.si.len - c * kChunk);
@@ -72,9 +73,10 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const BwdArgs &a,
     for (int m = 0; m < 8; ++m) {
       const uint32_t rq0 = (uint32_t)(32 * q_half(HW) + 4 * m + r16);
       const uint32_t rk0 = (uint32_t)(32 * k_half(HW) + 4 * m + r16);
-      R.buf[m] = bload16(rq, rq0 * rs + 16u * pc);
-      R.buf[8 + m] = bload16(rk, rk0 * rs + 16u * pc);
+      if (part & 1) R.buf[m] = bload16(rq, rq0 * rs + 16u * pc);
+      if (part & 2) R.buf[8 + m] = bload16(rk, rk0 * rs + 16u * pc);
     }
+    if (!(part & 1)) return;
   } else {
     const uint32_t rs = (uint32_t)(p.Hv * V * 2);
     const bf16 *ob = reinterpret_cast<const bf16 *>(a.dout) + (tok0 * p.Hv + it.h) * V;
@@ -169,11 +171,14 @@ __device__ __forceinline__ void helper_step(HelperRegs<HW> &Rc, HelperRegs<HW> &
                                             const BwdArgs &a, const Item &it, int c, char *smem,
                                             float *scratch, int lane) {
   const int c0 = it.sl.c_begin;
-  helper_load<HW>(Rl, a, it, max(c - 2, c0), lane);
+  // the P-tile roles issue their k rows after the commit the next barrier
+  // waits for, so that the loads issued ahead of it queue less
+  helper_load<HW>(Rl, a, it, max(c - 2, c0), lane, HW == 1 ? 3 : 1);
   const int cn = c - 1;
   helper_commit<HW>(Rc, reinterpret_cast<bf16 *>(smem + (cn & 1) * SET_BYTES),
                     reinterpret_cast<float *>(smem + 2 * SET_BYTES) + (cn & 1) * GATE_FLOATS,
                     scratch, a.p.scale, lane);
+  if (HW != 1) helper_load<HW>(Rl, a, it, max(c - 2, c0), lane, 2);
 }
 
 template <int HW>
