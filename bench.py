@@ -400,7 +400,8 @@ def main():
     # training keeps the per-chunk states from the forward for the backward
     # (one buffer, reused every step like an activation buffer)
     use_cache = not args.no_state_cache and not args.fwd_only
-    cache = (gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=args.cp)
+    cache = (gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=args.cp,
+                                   use_qk_l2norm_in_kernel=l2)
              if use_cache else None)
 
     def fwd(with_cache=use_cache, inference=False):

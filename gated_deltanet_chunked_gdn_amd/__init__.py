@@ -169,13 +169,16 @@ def plan_segments(q, k, v, cu_seqlens=None, cp_mode: int = -1) -> int:
     return int(n)
 
 
-def state_cache_empty(q, v, cu_seqlens=None, cp_mode: int = -1):
+def state_cache_empty(q, v, cu_seqlens=None, cp_mode: int = -1,
+                      use_qk_l2norm_in_kernel: bool = False):
     """An uninitialised state cache for this problem (an opaque uint8 buffer):
     chunk_gated_delta_rule_fwd fills it with the state entering every chunk
     and every chunk's T, and chunk_gated_delta_rule_bwd then takes those
     instead of recomputing them (memory for compute: 40 KB per chunk and
-    v-head at K = V = 128 in bf16)."""
-    pr = _Prepared(q, v, None, cu_seqlens, cp_mode)
+    v-head at K = V = 128 in bf16).  For calls with use_qk_l2norm_in_kernel
+    it also holds the normalised q, k rows and their factors, so pass the
+    same flag here."""
+    pr = _Prepared(q, v, None, cu_seqlens, cp_mode, use_qk_l2norm_in_kernel)
     n = lib().gdn_state_cache_size(pr.ref())
     if n == 0:
         raise ValueError(last_error())

@@ -207,18 +207,6 @@ gdn::FwdWorkspace fwd_layout(const gdn_problem_t *p, const gdn::Plan &pl, size_t
   off = align256(off + (size_t)pl.total_segs * p->Hv * kv);
   w.flags = off;
   off = align256(off + (size_t)pl.total_segs * p->Hv * 4);
-  if (p->qk_l2norm) {
-    const size_t rows = (size_t)pl.total_tokens * p->Hq;
-    w.l2 = true;
-    w.qn = off;
-    off = align256(off + rows * p->K * es);
-    w.kn = off;
-    off = align256(off + rows * p->K * es);
-    w.rq = off;
-    off = align256(off + rows * 4);
-    w.rk = off;
-    off = align256(off + rows * 4);
-  }
   w.total = off;
   return w;
 }
@@ -255,6 +243,7 @@ gdn::Problem to_problem(const gdn_problem_t *p) {
   q.dtype = p->dtype;
   q.scale = p->scale;
   q.cu = p->cu_seqlens;
+  q.l2 = p->qk_l2norm;
   return q;
 }
 
@@ -384,16 +373,35 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p) {
 
 // State cache layout: the per-chunk states ([chunks][Hv][K*V] in the lane layout, element
 // type), then at a 256-byte boundary the per-chunk T ([chunks][Hv][64][64]).
-static size_t cache_t_offset(const gdn_problem_t *p, const gdn::Plan &pl) {
+// Byte offsets of the state cache's pieces: the states, T, and with qk_l2norm
+// the normalised q, k rows and their factors.
+struct CacheLayout {
+  size_t t = 0, qn = 0, kn = 0, rq = 0, rk = 0, total = 0;
+};
+static CacheLayout cache_layout(const gdn_problem_t *p, const gdn::Plan &pl) {
   const size_t es = p->dtype == GDN_BF16 ? 2 : 4;
-  return align256((size_t)pl.total_chunks * p->Hv * p->K * p->V * es);
+  CacheLayout c;
+  c.t = align256((size_t)pl.total_chunks * p->Hv * p->K * p->V * es);
+  size_t off = c.t + (size_t)pl.total_chunks * p->Hv * 64 * 64 * es;
+  if (p->qk_l2norm) {
+    const size_t rows = (size_t)pl.total_tokens * p->Hq;
+    c.qn = off = align256(off);
+    off += rows * p->K * es;
+    c.kn = off = align256(off);
+    off += rows * p->K * es;
+    c.rq = off = align256(off);
+    off += rows * 4;
+    c.rk = off = align256(off);
+    off += rows * 4;
+  }
+  c.total = off;
+  return c;
 }
 
 size_t gdn_state_cache_size(const gdn_problem_t *p) {
   gdn::Plan pl;
   if (validate(p, &pl) != GDN_OK) return 0;
-  const size_t es = p->dtype == GDN_BF16 ? 2 : 4;
-  const size_t n = cache_t_offset(p, pl) + (size_t)pl.total_chunks * p->Hv * 64 * 64 * es;
+  const size_t n = cache_layout(p, pl).total;
   return n > 0 ? n : 256;  // a valid size even for an empty problem
 }
 
@@ -444,20 +452,20 @@ int fwd_run(const gdn_problem_t *p, const gdn::Plan &pl, const gdn::FwdWorkspace
   a.A = A;
   a.h = h;
   a.h_e = state_cache;  // the segment passes store the states they run through
-  if (state_cache) a.tm_ext = static_cast<char *>(state_cache) + cache_t_offset(p, pl);
+  if (state_cache) {
+    char *sc = static_cast<char *>(state_cache);
+    const CacheLayout cl = cache_layout(p, pl);
+    a.tm_ext = sc + cl.t;
+    if (p->qk_l2norm && pl.total_tokens > 0) {
+      a.qn_out = sc + cl.qn;
+      a.kn_out = sc + cl.kn;
+      a.rq_out = reinterpret_cast<float *>(sc + cl.rq);
+      a.rk_out = reinterpret_cast<float *>(sc + cl.rk);
+    }
+  }
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
-  hipError_t e = hipSuccess;
-  if (wl.l2 && pl.total_tokens > 0) {
-    // every kernel then reads the normalised rows
-    e = gdn::launch_l2norm(a.p, pl.total_tokens, q, k, a.ws + wl.qn, a.ws + wl.kn,
-                           reinterpret_cast<float *>(a.ws + wl.rq),
-                           reinterpret_cast<float *>(a.ws + wl.rk),
-                           static_cast<hipStream_t>(stream));
-    a.q = a.ws + wl.qn;
-    a.k = a.ws + wl.kn;
-  }
-  if (e == hipSuccess) e = gdn::launch_fwd(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = gdn::launch_fwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return GDN_OK;
@@ -528,21 +536,22 @@ int gdn_chunk_bwd(const gdn_problem_t *p, const void *q, const void *k, const vo
   a.dg = dg;
   a.dh0 = dh0;
   a.hcache = state_cache;
-  if (state_cache) a.tm_ext = static_cast<const char *>(state_cache) + cache_t_offset(p, pl);
+  if (state_cache) {
+    const char *sc = static_cast<const char *>(state_cache);
+    const CacheLayout cl = cache_layout(p, pl);
+    a.tm_ext = sc + cl.t;
+    if (p->qk_l2norm && pl.total_tokens > 0) {
+      // the rows the forward normalised, and their factors for dq, dk
+      a.q = sc + cl.qn;
+      a.k = sc + cl.kn;
+      a.rq = reinterpret_cast<const float *>(sc + cl.rq);
+      a.rk = reinterpret_cast<const float *>(sc + cl.rk);
+      a.p.l2 = 0;
+    }
+  }
   a.ws = static_cast<char *>(workspace);
   a.wl = wl;
-  hipError_t e = hipSuccess;
-  if (wl.fwd.l2 && pl.total_tokens > 0) {
-    e = gdn::launch_l2norm(a.p, pl.total_tokens, q, k, a.ws + wl.fwd.qn, a.ws + wl.fwd.kn,
-                           reinterpret_cast<float *>(a.ws + wl.fwd.rq),
-                           reinterpret_cast<float *>(a.ws + wl.fwd.rk),
-                           static_cast<hipStream_t>(stream));
-    a.q = a.ws + wl.fwd.qn;
-    a.k = a.ws + wl.fwd.kn;
-    a.rq = reinterpret_cast<const float *>(a.ws + wl.fwd.rq);
-    a.rk = reinterpret_cast<const float *>(a.ws + wl.fwd.rk);
-  }
-  if (e == hipSuccess) e = gdn::launch_bwd(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = gdn::launch_bwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return GDN_OK;

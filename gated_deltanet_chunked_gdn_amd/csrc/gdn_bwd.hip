@@ -57,7 +57,7 @@ struct RSmem {
 
 template <typename E, int K, int V, bool MAIN>
 __device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem &S, float scale,
-                                           int tid = threadIdx.x) {
+                                           bool l2, int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
   using L = RevLds<E, K, V>;
   E *sm = reinterpret_cast<E *>(S.base);
@@ -65,10 +65,12 @@ __device__ __forceinline__ void rev_commit(const Pref<E, K, V> &pf, const RSmem 
 #pragma unroll
   for (int m = 0; m < G::NQ; ++m) {
     const int idx = tid + kThreads * m;
+    const uint4 xq = l2 ? l2n_piece<E, PK>(pf.q[m]) : pf.q[m];
+    const uint4 xk = l2 ? l2n_piece<E, PK>(pf.k[m]) : pf.k[m];
     if (idx < G::PQ) {
       const int r = idx / PK, cv = idx % PK;
-      *reinterpret_cast<uint4 *>(sm + L::oQ + r * G::LDK + cv * G::VEC) = pf.q[m];
-      *reinterpret_cast<uint4 *>(sm + L::oK + r * G::LDK + cv * G::VEC) = pf.k[m];
+      *reinterpret_cast<uint4 *>(sm + L::oQ + r * G::LDK + cv * G::VEC) = xq;
+      *reinterpret_cast<uint4 *>(sm + L::oK + r * G::LDK + cv * G::VEC) = xk;
     }
   }
   // dO and T stay row-major; their transposed operands come from LDS
@@ -149,7 +151,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
     const int c = c_end - 1;
     pref_load<E, K, V, MAIN>(pf, p, qp, kp, dop, tmat, a.g, bp, si.tok0 + (int64_t)c * kChunk,
                              min(kChunk, si.len - c * kChunk), h, chunk_gid0 + c);
-    rev_commit<E, K, V, MAIN>(pf, S, scale);
+    rev_commit<E, K, V, MAIN>(pf, S, scale, p.l2);
     tiles_to_lds_t<E, K, V>(st, sDt);
   }
   __syncthreads();
@@ -311,7 +313,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
       __syncthreads();
     }
     if (c - 1 >= c_begin && !zero_exit) {
-      rev_commit<E, K, V, MAIN>(pf, S, scale, tid);
+      rev_commit<E, K, V, MAIN>(pf, S, scale, p.l2, tid);
       __syncthreads();
     }
   }
@@ -478,6 +480,7 @@ struct LocSmall {
   float bet[64];
   float rowp[4][2][64];  // [de, db, rs, c][half][row]
   float colp[4][64];     // [row tile][col]
+  float rq[64], rk[64];  // L2-normalisation factors of the item's q, k rows
   float glp[kNW];
 };
 
@@ -717,10 +720,17 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = 0; m < NQP; ++m) {
     const int idx = tid + kThreads * m;
+    float fq = 0.f, fk = 0.f;
+    const uint4 xq = p.l2 ? l2n_piece<E, PK>(zq[m], fq) : zq[m];
+    const uint4 xk = p.l2 ? l2n_piece<E, PK>(zk[m], fk) : zk[m];
     if (idx < 64 * PK) {
       const int r = idx / PK, cv = idx % PK;
-      *reinterpret_cast<uint4 *>(sQ + r * C::LDK + cv * VEC) = zq[m];
-      *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = zk[m];
+      *reinterpret_cast<uint4 *>(sQ + r * C::LDK + cv * VEC) = xq;
+      *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = xk;
+      if (cv == 0) {
+        ls.rq[r] = fq;
+        ls.rk[r] = fk;
+      }
     }
   }
 #pragma unroll
@@ -1127,7 +1137,7 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
   // normalised rows x_hat = x r (held in sQ, sK); back to the raw rows,
   // dx = r (dx_hat - x_hat <x_hat, dx_hat>), the row dot taken over K (this
   // wave's columns, then both column halves through LDS)
-  if (a.rq) {
+  if (p.l2 || a.rq) {
     relane();
     f32x4 xq[NCHK], xk[NCHK];
     float pq[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1157,8 +1167,8 @@ __global__ __launch_bounds__(kThreads) void local_grad_kernel(BwdArgs a) {
       const float tk = rowp[1][0][s] + rowp[1][1][s];
       float fq = 0.f, fk = 0.f;
       if (s < rows) {
-        fq = a.rq[(tok0 + s) * p.Hq + hq];
-        fk = a.rk[(tok0 + s) * p.Hq + hq];
+        fq = p.l2 ? ls.rq[s] : a.rq[(tok0 + s) * p.Hq + hq];
+        fk = p.l2 ? ls.rk[s] : a.rk[(tok0 + s) * p.Hq + hq];
       }
 #pragma unroll
       for (int m = 0; m < NCHK; ++m) {

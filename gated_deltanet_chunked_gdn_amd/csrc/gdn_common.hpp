@@ -195,6 +195,26 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void buf_store16(const uint4 &x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, r, (int)off, 0, 0);
 }
+// Loads through such a buffer: past the range they read 0 without touching
+// memory, so guarded loads need no branch (a load under a branch makes the
+// compiler wait for it where the branches join, right after its issue).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base, uint32_t bytes) {
+  return raw_buffer(const_cast<void *>(base), bytes);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+template <typename E>
+__device__ __forceinline__ E buf_load_elem(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ float buf_load_elem<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+template <>
+__device__ __forceinline__ bf16 buf_load_elem<bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -242,6 +262,37 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_mov<0x124>(x);  // row_ror:4
   x += dpp_mov<0x128>(x);  // row_ror:8
   return x;
+}
+
+// Sum over aligned groups of LPR lanes (LPR = 2, 4, 8 or 16, inside a row):
+// swap neighbours, then pairs inside quads, then quads (mirror inside each
+// half row), then halves (row mirror).  The two partners of every exchange
+// hold equal partial sums, so every lane of a group ends with the same value.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16, "lanes per group");
+  x += dpp_mov<0xB1>(x);                   // quad_perm [1,0,3,2]
+  if (LPR >= 4) x += dpp_mov<0x4E>(x);     // quad_perm [2,3,0,1]
+  if (LPR >= 8) x += dpp_mov<0x141>(x);    // row_half_mirror
+  if (LPR >= 16) x += dpp_mov<0x140>(x);   // row_mirror
+  return x;
+}
+
+// The optional in-library L2 normalisation of q and k rows, applied where a
+// kernel moves the rows it has loaded into LDS: x is one 16-byte piece of a
+// row whose LPR pieces are held by LPR consecutive lanes.  Returns the piece
+// times r = (sum of the row's squares + 1e-6)^(-1/2), rounded once; r is
+// also returned (the same in every lane of the row).
+template <typename E, int LPR>
+__device__ __forceinline__ uint4 l2n_piece(const uint4 &x, float &r) {
+  const float ss = group_sum<LPR>(dot_piece<E>(x, x, 0.f));
+  r = 1.0f / __builtin_sqrtf(ss + 1e-6f);
+  return scale_piece<E>(x, r);
+}
+template <typename E, int LPR>
+__device__ __forceinline__ uint4 l2n_piece(const uint4 &x) {
+  float r;
+  return l2n_piece<E, LPR>(x, r);
 }
 
 // Lane 63's value of x, as a wave-uniform float.

@@ -120,7 +120,10 @@ __device__ __forceinline__ void put16(float *dst, int ld, f32x4 c, float sgn) {
 // head (the second wave idles when there is one v-head per q/k head).
 constexpr int kPrepThreads = 128;
 
-template <typename E, int K>
+// WN: the normalised q and k rows of every item, and their factors, are
+// written out (in-library L2 normalisation with a state cache): the passes
+// after this one and the backward read those rows.
+template <typename E, int K, bool WN>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2))) void prep_kernel(
     FwdArgs a) {
   using C = PrepCfg<E, K>;
@@ -154,34 +157,41 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
   // stays in the element type until used, so nothing waits for the load)
   float gv_n = 0.f;
   E bv_n = from_f32<E>(0.f);
-  auto load_gb = [&](const Item &x, int hl) {
-    gv_n = 0.f;
-    bv_n = from_f32<E>(0.f);
-    if (hl < G && lane < x.rows) {
-      const int64_t gi = (x.tok0 + lane) * p.Hv + x.hq * G + hl;
-      gv_n = a.g[gi];
-      bv_n = reinterpret_cast<const E *>(a.beta)[gi];
-    }
+  auto load_gb = [&](const Item &x, int hl, bool on) {
+    const int64_t g0 = x.tok0 * p.Hv + x.hq * G + hl;
+    const uint32_t rs = (uint32_t)p.Hv;
+    const uint32_t n = on && hl < G ? (uint32_t)x.rows * rs : 0u;
+    const auto rg = raw_buffer(a.g + g0, n * 4u);
+    const auto rb = raw_buffer(reinterpret_cast<const E *>(a.beta) + g0, n * (uint32_t)sizeof(E));
+    gv_n = buf_load_elem<float>(rg, (uint32_t)lane * rs * 4u);
+    bv_n = buf_load_elem<E>(rb, (uint32_t)lane * rs * (uint32_t)sizeof(E));
   };
   const E *kp = reinterpret_cast<const E *>(a.k);
+  const E *qp = reinterpret_cast<const E *>(a.q);
   constexpr int VEC = 16 / (int)sizeof(E);
   constexpr int PR = K / VEC;
   constexpr int NP = (64 * PR + kPrepThreads - 1) / kPrepThreads;  // 16-byte pieces a thread
-  uint4 kv[NP];
-  auto load_k = [&](const Item &x) {
+  static_assert(64 * PR % kPrepThreads == 0, "whole rows a thread");
+  constexpr int NQV = WN ? NP : 1;
+  uint4 kv[NP], qv[NQV];
+  const uint32_t qk_rs = (uint32_t)(p.Hq * K * sizeof(E));  // bytes between token rows
+  // (the loads are unconditional: with on = false their range is empty)
+  auto load_k = [&](const Item &x, bool on) {
+    const int64_t e0 = (x.tok0 * p.Hq + x.hq) * K;
+    const uint32_t n = on ? (uint32_t)x.rows * qk_rs : 0u;  // rows past the chunk read 0
+    const auto rk = raw_buffer(kp + e0, n), rq = raw_buffer(qp + e0, n);
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
       const int idx = tid + kPrepThreads * m;
-      const int r = idx / PR, cv = idx % PR;
-      kv[m] = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < 64 * PR && r < x.rows)
-        kv[m] = *reinterpret_cast<const uint4 *>(kp + ((x.tok0 + r) * p.Hq + x.hq) * K + cv * VEC);
+      const uint32_t off = (uint32_t)(idx / PR) * qk_rs + (uint32_t)(idx % PR) * 16u;
+      kv[m] = buf_load16(rk, off);
+      if (WN) qv[m] = buf_load16(rq, off);
     }
   };
   if (blockIdx.x >= n_items) return;
   Item cur = item_of(blockIdx.x);
-  load_gb(cur, w);
-  load_k(cur);
+  load_gb(cur, w, true);
+  load_k(cur, true);
   E *tmat = reinterpret_cast<E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat);
   constexpr int LD = 17, BS = C::BS;
   float *W = reinterpret_cast<float *>(smem) + w * C::floatsW;
@@ -196,12 +206,27 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
     const bool has_next = it_next < n_items;
     const int hq = cur.hq, rows = cur.rows;
     const int64_t gid = cur.gid, tok0 = cur.tok0;
-    // the k tile into LDS (the per-wave buffers that alias it are free)
+    // the k tile into LDS (the per-wave buffers that alias it are free);
+    // normalised rows out through buffers that end with the chunk's rows
+    const int64_t e0 = (tok0 * p.Hq + hq) * K;
+    const uint32_t nb = (uint32_t)rows * qk_rs;
+    const auto wq = raw_buffer(reinterpret_cast<E *>(a.qn_out) + e0, WN ? nb : 0u);
+    const auto wk = raw_buffer(reinterpret_cast<E *>(a.kn_out) + e0, WN ? nb : 0u);
+    const auto wrq = raw_buffer(a.rq_out + tok0 * p.Hq + hq, WN ? (uint32_t)rows * p.Hq * 4u : 0u);
+    const auto wrk = raw_buffer(a.rk_out + tok0 * p.Hq + hq, WN ? (uint32_t)rows * p.Hq * 4u : 0u);
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
       const int idx = tid + kPrepThreads * m;
       const int r = idx / PR, cv = idx % PR;
-      if (idx < 64 * PR) *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = kv[m];
+      float fk = 0.f;
+      const uint4 x = (WN || p.l2) ? l2n_piece<E, PR>(kv[m], fk) : kv[m];
+      *reinterpret_cast<uint4 *>(sK + r * C::LDK + cv * VEC) = x;
+      if (WN) {
+        buf_store16(x, wk, (uint32_t)r * qk_rs + (uint32_t)cv * 16u);
+        if (cv == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, fk), wrk,
+                                                (int)((uint32_t)r * p.Hq * 4u), 0, 0);
+      }
     }
     __syncthreads();
     f32x4 kk[10];
@@ -224,20 +249,37 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
           for (int ct = 0; ct <= rt; ++ct, ++t) kk[t] = M::mma(x[rt], x[ct], kk[t]);
       }
     }
-    __syncthreads();  // the per-wave buffers alias sK
-    Item nxt = cur;
-    if (has_next) {
-      nxt = item_of(it_next);
-      load_k(nxt);
+    if (WN) {
+      // the q rows (their work overlaps the products above)
+#pragma unroll
+      for (int m = 0; m < NQV; ++m) {
+        const int idx = tid + kPrepThreads * m;
+        const int r = idx / PR, cv = idx % PR;
+        float fq;
+        const uint4 y = l2n_piece<E, PR>(qv[m], fq);
+        buf_store16(y, wq, (uint32_t)r * qk_rs + (uint32_t)cv * 16u);
+        if (cv == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, fq), wrq,
+                                                (int)((uint32_t)r * p.Hq * 4u), 0, 0);
+      }
     }
+    __syncthreads();  // the per-wave buffers alias sK
+    const Item nxt = has_next ? item_of(it_next) : cur;
+    load_k(nxt, has_next);
     for (int hl = w; hl < G; hl += nw) {
       const int h = hq * G + hl;
       const int64_t gi = (tok0 + lane) * p.Hv + h;
       const float gv = gv_n, bv = to_f32(bv_n);
-      if (hl + nw < G)
-        load_gb(cur, hl + nw);
-      else if (has_next)
-        load_gb(nxt, w);
+      {
+        // this wave's next v-head: in this item, else the next item's first
+        const bool in_item = hl + nw < G;
+        Item x;
+        x.hq = in_item ? cur.hq : nxt.hq;
+        x.rows = in_item ? cur.rows : nxt.rows;
+        x.gid = in_item ? cur.gid : nxt.gid;
+        x.tok0 = in_item ? cur.tok0 : nxt.tok0;
+        load_gb(x, in_item ? hl + nw : w, in_item || has_next);
+      }
       const float gam = wave_incl_scan(gv);
       float *sG = W + C::fG, *sB = W + C::fB;
       sG[lane] = gam * kLog2e;
@@ -440,7 +482,7 @@ struct Smem {
 };
 
 template <typename E, int K, int V, bool WANT_V>
-__device__ __forceinline__ void fwd_commit(const Pref<E, K, V> &pf, const Smem &S,
+__device__ __forceinline__ void fwd_commit(const Pref<E, K, V> &pf, const Smem &S, bool l2,
                                            int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
   using L = FwdLds<E, K, V>;
@@ -449,10 +491,12 @@ __device__ __forceinline__ void fwd_commit(const Pref<E, K, V> &pf, const Smem &
 #pragma unroll
   for (int m = 0; m < G::NQ; ++m) {
     const int idx = tid + kThreads * m;
+    const uint4 xq = l2 ? l2n_piece<E, PK>(pf.q[m]) : pf.q[m];
+    const uint4 xk = l2 ? l2n_piece<E, PK>(pf.k[m]) : pf.k[m];
     if (idx < G::PQ) {
       const int r = idx / PK, cv = idx % PK;
-      *reinterpret_cast<uint4 *>(sm + L::oQ + r * G::LDK + cv * G::VEC) = pf.q[m];
-      *reinterpret_cast<uint4 *>(sm + L::oK + r * G::LDK + cv * G::VEC) = pf.k[m];
+      *reinterpret_cast<uint4 *>(sm + L::oQ + r * G::LDK + cv * G::VEC) = xq;
+      *reinterpret_cast<uint4 *>(sm + L::oK + r * G::LDK + cv * G::VEC) = xk;
     }
   }
   if (WANT_V) {
@@ -525,7 +569,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
     pref_load<E, K, V, WANT_V>(pf, p, qp, kp, vp, tmat, a.g, bp,
                                si.tok0 + (int64_t)c_begin * kChunk, rows, h,
                                chunk_gid0 + c_begin);
-    fwd_commit<E, K, V, WANT_V>(pf, S);
+    fwd_commit<E, K, V, WANT_V>(pf, S, p.l2);
     tiles_to_lds_t<E, K, V>(st, sSt);
   }
   __syncthreads();
@@ -769,7 +813,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
       }
     }
     if (c + 1 < c_end && !zero_exit) {
-      fwd_commit<E, K, V, WANT_V>(pf, S, tid);
+      fwd_commit<E, K, V, WANT_V>(pf, S, p.l2, tid);
       __syncthreads();
     }
   }
@@ -907,7 +951,10 @@ static void launch_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
   const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (int64_t)lds));
   const int64_t grid = std::min<int64_t>(items, per_cu * (pl.cus > 0 ? pl.cus : 256));
   KernelTimer kt("prep", st);
-  prep_kernel<E, K><<<dim3((unsigned)grid), kPrepThreads, lds, st>>>(a);
+  if (p.l2 && a.qn_out)
+    prep_kernel<E, K, true><<<dim3((unsigned)grid), kPrepThreads, lds, st>>>(a);
+  else
+    prep_kernel<E, K, false><<<dim3((unsigned)grid), kPrepThreads, lds, st>>>(a);
 }
 
 // GDN_FWD_SLICE=0 in the environment runs pass 1 on the general segment
@@ -936,6 +983,14 @@ static hipError_t launch_fwd_t(const FwdArgs &a, const float *Ain, hipStream_t s
   }
   if ((stages & kStageT) && pl.total_chunks > 0) launch_prep<E, K>(a, Ain, st);
   if (!(stages & kStageSegs)) return hipGetLastError();
+  if (a.qn_out && a.p.l2 && (stages & kStageT)) {
+    // prep has written the normalised rows: the passes read those
+    FwdArgs b = a;
+    b.q = a.qn_out;
+    b.k = a.kn_out;
+    b.p.l2 = 0;
+    return launch_fwd_t<E, K, V, WRITE_O>(b, Ain, st, stages & kStageSegs);
+  }
   if (pl.total_chunks > 0) {
     if (WRITE_O && fwd_slice_supported(a) && !slice_disabled()) {
       const hipError_t e = launch_fwd_slice_main(a, st);
@@ -992,63 +1047,6 @@ hipError_t launch_bwd_prep(const FwdArgs &a, const float *Ain, hipStream_t st) {
 // Forward state recompute for the backward: states only (a.h_e), no output.
 hipError_t launch_fwd_states(const FwdArgs &a, hipStream_t st) {
   return dispatch_kv<false>(a, nullptr, st, kStageSegs);
-}
-
-// ------------------------------------------------- in-library L2 normalisation
-// Rows of K elements (one token, one q/k head) of q then k: each thread holds
-// one 16-byte piece and the LPR consecutive lanes of a row combine their sums
-// of squares.  x_hat = x r (rounded once to E), r = (sum x^2 + 1e-6)^-1/2.
-template <typename E, int K>
-__global__ __launch_bounds__(256) void l2norm_kernel(const E *__restrict__ q,
-                                                      const E *__restrict__ k, E *qn, E *kn,
-                                                      float *rq, float *rk, int64_t rows) {
-  constexpr int VEC = 16 / (int)sizeof(E);
-  constexpr int LPR = K / VEC;  // lanes per row: 2 .. 16, divides 64
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = t / LPR;
-  const int part = (int)(t % LPR);
-  const bool active = row < 2 * rows;
-  const bool is_k = row >= rows;
-  const int64_t r = is_k ? row - rows : row;
-  const uint32_t off = (uint32_t)part * 16u;
-  uint4 x = make_uint4(0u, 0u, 0u, 0u);
-  if (active)
-    x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>((is_k ? k : q) + r * K) +
-                                         off);
-  float ss = dot_piece<E>(x, x, 0.f);
-#pragma unroll
-  for (int o = 1; o < LPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
-  const float f = 1.0f / __builtin_sqrtf(ss + 1e-6f);
-  if (active) {
-    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>((is_k ? kn : qn) + r * K) + off) =
-        scale_piece<E>(x, f);
-    if (part == 0) (is_k ? rk : rq)[r] = f;
-  }
-}
-
-hipError_t launch_l2norm(const Problem &p, int64_t tokens, const void *q, const void *k,
-                         void *qn, void *kn, float *rq, float *rk, hipStream_t st) {
-  const int64_t rows = tokens * p.Hq;
-  KernelTimer kt("l2norm", st);
-#define GDN_L2(E, KK)                                                                      \
-  if (p.K == KK) {                                                                        \
-    constexpr int LPR = KK * (int)sizeof(E) / 16;                                         \
-    const int64_t threads = 2 * rows * LPR;                                               \
-    l2norm_kernel<E, KK><<<dim3((unsigned)((threads + 255) / 256)), 256, 0, st>>>(          \
-        static_cast<const E *>(q), static_cast<const E *>(k), static_cast<E *>(qn),        \
-        static_cast<E *>(kn), rq, rk, rows);                                              \
-    return hipGetLastError();                                                              \
-  }
-  if (p.dtype == 1) {
-    GDN_L2(bf16, 32)
-    GDN_L2(bf16, 64)
-    GDN_L2(bf16, 128)
-  } else {
-    GDN_L2(float, 32)
-    GDN_L2(float, 64)
-  }
-#undef GDN_L2
-  return hipErrorInvalidValue;
 }
 
 }  // namespace gdn

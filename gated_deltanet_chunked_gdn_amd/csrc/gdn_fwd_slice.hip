@@ -133,7 +133,7 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const FwdArgs &a,
 // Writes the chunk held in R into buffer set `set` (role HW's share).
 template <int HW>
 __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set, float *gates,
-                                              float *scratch, int lane) {
+                                              float *scratch, bool l2, int lane) {
   const int h = lane >> 5, r32 = lane & 31, r16 = lane >> 4, pc = lane & 15;
   const float gam = wave_incl_scan(R.g) * kLog2e;  // gate cumsum, times log2(e)
   if (HW != 1) {
@@ -143,8 +143,10 @@ __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set
     // q and k rows of this half into the pi layout
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      put_pi(set + oQ + (32 * rbq + 4 * m + r16) * PITCH, pc, R.buf[m]);
-      put_pi(set + oK + (32 * rbk + 4 * m + r16) * PITCH, pc, R.buf[8 + m]);
+      const uint4 xq = l2 ? l2n_piece<bf16, 16>(R.buf[m]) : R.buf[m];
+      const uint4 xk = l2 ? l2n_piece<bf16, 16>(R.buf[8 + m]) : R.buf[8 + m];
+      put_pi(set + oQ + (32 * rbq + 4 * m + r16) * PITCH, pc, xq);
+      put_pi(set + oK + (32 * rbk + 4 * m + r16) * PITCH, pc, xk);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -231,7 +233,7 @@ __device__ __forceinline__ void helper_step(HelperRegs<HW> &Rc, HelperRegs<HW> &
   const int cn = c + 1;
   helper_commit<HW>(Rc, reinterpret_cast<bf16 *>(smem + (cn & 1) * SET_BYTES),
                     reinterpret_cast<float *>(smem + 2 * SET_BYTES) + (cn & 1) * GATE_FLOATS,
-                    scratch, lane);
+                    scratch, a.p.l2, lane);
   if (HW == 1) helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane);
   if (HW != 1) helper_load<HW>(Rl, a, it, min(c + 2, c1 - 1), lane, 2);
 }
@@ -246,7 +248,7 @@ __device__ __forceinline__ void helper_loop(const FwdArgs &a, const Item &it, ch
     helper_load<HW>(R1, a, it, min(c0 + 1, c1 - 1), lane);
     helper_commit<HW>(R0, reinterpret_cast<bf16 *>(smem + (c0 & 1) * SET_BYTES),
                       reinterpret_cast<float *>(smem + 2 * SET_BYTES) + (c0 & 1) * GATE_FLOATS,
-                      scratch, lane);
+                      scratch, a.p.l2, lane);
   }
   __syncthreads();
   // R1 holds chunk c + 1 at even steps (from c0), R0 at odd ones

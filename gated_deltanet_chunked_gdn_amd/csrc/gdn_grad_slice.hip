@@ -88,6 +88,8 @@ struct Small {
   float rsA[3][32], csA[3][32];  // of beta (-dA) E KK
   float dbA[3][32];              // row sums of (-dA) E KK
   float gl[8];                   // <D, S> per wave
+  // in-library q/k L2 normalisation: the item's row factors
+  float rq[64], rk[64];
 };
 constexpr int LDS_BYTES = oF + (int)sizeof(Small);
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -141,6 +143,7 @@ __device__ __forceinline__ GItem pick(bool first, const GItem &x, const GItem &y
 struct Pref {
   uint4 s[2], d[2], o, v, t, q[2], k[2];
   float g, b;
+  float fr;  // waves 5, 6: the q (k) row factor of lane's row (rows normalised upstream)
 };
 
 struct Ctx {
@@ -236,6 +239,14 @@ __device__ __forceinline__ void load_qk(Pref &pf, const BwdArgs &a, const GItem 
     pf.q[m] = slice::bload16(rq, off);
     pf.k[m] = slice::bload16(rk, off);
   }
+  // rows normalised upstream: their factors (wave 5 for q, wave 6 for k;
+  // empty ranges elsewhere)
+  const bool fw = a.rq && (c.w == 5 || c.w == 6) && on;
+  const float *fb = (c.w == 5 ? a.rq : a.rk);
+  const auto rf = slice::rsrc_of(fb ? fb + x.tok0 * p.Hq + x.hq : nullptr,
+                                 fw ? (uint32_t)(x.rows * p.Hq * 4) : 0u);
+  pf.fr = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(rf, (int)(c.lane * p.Hq * 4), 0, 0));
 }
 
 // The block's inputs into LDS.  A 16-byte piece of the states' lane layout
@@ -258,13 +269,24 @@ __device__ __forceinline__ void commit_block(const Pref &pf, const Ctx &c, float
 __device__ __forceinline__ void commit_head(const Pref &pf, const Ctx &c) {
   put_pi(c.bf(oT) + (c.tid >> 3) * P64, c.tid & 7, pf.t);
 }
-__device__ __forceinline__ void commit_qk(const Pref &pf, const Ctx &c) {
+// (with in-library L2 normalisation the rows are normalised on the way, and
+// their factors kept for the chain rule of dq, dk; rows normalised upstream
+// come with their factors)
+__device__ __forceinline__ void commit_qk(const Pref &pf, const Ctx &c, bool l2) {
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int ci = c.tid + kThr * m;
-    put_pi(c.bf(oQ) + (ci >> 4) * P128, ci & 15, pf.q[m]);
-    put_pi(c.bf(oK) + (ci >> 4) * P128, ci & 15, pf.k[m]);
+    float fq = 0.f, fk = 0.f;
+    const uint4 xq = l2 ? l2n_piece<bf16, 16>(pf.q[m], fq) : pf.q[m];
+    const uint4 xk = l2 ? l2n_piece<bf16, 16>(pf.k[m], fk) : pf.k[m];
+    put_pi(c.bf(oQ) + (ci >> 4) * P128, ci & 15, xq);
+    put_pi(c.bf(oK) + (ci >> 4) * P128, ci & 15, xk);
+    if (l2 && (ci & 15) == 0) {
+      c.sm().rq[ci >> 4] = fq;
+      c.sm().rk[ci >> 4] = fk;
+    }
   }
+  if (!l2 && (c.w == 5 || c.w == 6)) (c.w == 5 ? c.sm().rq : c.sm().rk)[c.lane] = pf.fr;
 }
 // one wave: cumulative gates of the chunk (lane = row) into gate set `set`
 __device__ __forceinline__ void commit_gates(const Pref &pf, const Ctx &c, int set) {
@@ -511,6 +533,58 @@ __device__ __forceinline__ void e_tiles_out(const f32x16 (&eacc)[2], const f32x1
   }
 }
 
+// In-library L2 normalisation: dq, dk so far are gradients with respect to
+// the normalised rows x_hat = x r; back to the raw rows,
+// dx = r (dx_hat - x_hat <x_hat, dx_hat>).  The dq, dk waves put dx_hat into
+// LDS in fp32 (rows of pitch F32P floats, over regions that are free at the
+// end of an item); then every thread takes one 8-column piece of a q row and
+// of a k row, forms the row dot over the 16 lanes that hold the row, and
+// writes dx.
+constexpr int F32P = 132;
+constexpr int oFQ = oS, oFK = oO;
+static_assert(64 * F32P * 4 <= oO - oS && 64 * F32P * 4 <= oPEt - oO, "fp32 staging");
+__device__ __forceinline__ void stage_f32(const f32x16 (&x)[2], int off, int rt, int kp,
+                                          const Ctx &c) {
+  float *f = reinterpret_cast<float *>(c.smem + off);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = 32 * (2 * kp + j) + c.r32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[(32 * rt + acc_row(i, c.h)) * F32P + col] = x[j][i];
+  }
+}
+// piece pc (columns 8 pc .. 8 pc + 7) of a pi-layout bf16 row, in natural order
+__device__ __forceinline__ uint4 get_pi(const bf16 *row, int pc) {
+  const int blk = (8 * pc) & ~15, q0 = 2 * (pc & 1);
+  const uint2 lo = *reinterpret_cast<const uint2 *>(row + blk + 4 * slice::pi4(q0));
+  const uint2 hi = *reinterpret_cast<const uint2 *>(row + blk + 4 * slice::pi4(q0 + 1));
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+__device__ __forceinline__ uint4 l2_back(const bf16 *xrow, const float *drow, float r, int pc) {
+  const uint4 xp = get_pi(xrow, pc);
+  const bf16 *xh = reinterpret_cast<const bf16 *>(&xp);
+  const f32x4 d0 = *reinterpret_cast<const f32x4 *>(drow + 8 * pc);
+  const f32x4 d1 = *reinterpret_cast<const f32x4 *>(drow + 8 * pc + 4);
+  float d[8], x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    d[e] = d0[e];
+    d[4 + e] = d1[e];
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = (float)xh[e];
+    t += x[e] * d[e];
+  }
+  t = group_sum<16>(t);
+  uint4 out;
+  bf16 *o = reinterpret_cast<bf16 *>(&out);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (bf16)(r * (d[e] - x[e] * t));
+  return out;
+}
+
 // dq += (dP * E) K;  dk += (dP * E)^T Q + (dKK + dKK^T) K  (dq, dk waves)
 __device__ __forceinline__ void e_products(f32x16 (&dq)[2], f32x16 (&dk)[2], int rt, int kp,
                                            const Ctx &c) {
@@ -569,7 +643,7 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
     c.relane();
     // ---- item start: q, k, the first v-head's T and gates
     __syncthreads();
-    commit_qk(pf, c);
+    commit_qk(pf, c, p.l2);
     commit_head(pf, c);
     if (c.w == 7) commit_gates(pf, c, u & 1);
     __syncthreads();
@@ -848,15 +922,21 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
     if constexpr (!R::kV) e_products(dq, dk, rt, kp, c);
     if constexpr (ROLE == 1) store_gates(a, cur, Gq - 1, (u - 1) & 1, c);
     __syncthreads();
+    const bool l2 = p.l2 || a.rq;
     if constexpr (!R::kV) {
+      if (l2) {
+        stage_f32(dq, oFQ, rt, kp, c);
+        stage_f32(dk, oFK, rt, kp, c);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = 32 * (2 * kp + j) + c.r32;
+        for (int j = 0; j < 2; ++j) {
+          const int col = 32 * (2 * kp + j) + c.r32;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = 32 * rt + acc_row(i, c.h);
-          c.bf(oQ)[row * P128 + col] = (bf16)dq[j][i];
-          c.bf(oK)[row * P128 + col] = (bf16)dk[j][i];
+          for (int i = 0; i < 16; ++i) {
+            const int row = 32 * rt + acc_row(i, c.h);
+            c.bf(oQ)[row * P128 + col] = (bf16)dq[j][i];
+            c.bf(oK)[row * P128 + col] = (bf16)dk[j][i];
+          }
         }
       }
     }
@@ -871,8 +951,18 @@ __device__ void run(const BwdArgs &a, const Ctx &c0) {
         const int ci = c.tid + kThr * m;
         const int r = ci >> 4, pc16 = ci & 15;
         const uint32_t off = (uint32_t)r * qk_rs + (uint32_t)pc16 * 16u;
-        buf_store16(*reinterpret_cast<const uint4 *>(c.bf(oQ) + r * P128 + 8 * pc16), rq, off);
-        buf_store16(*reinterpret_cast<const uint4 *>(c.bf(oK) + r * P128 + 8 * pc16), rk, off);
+        uint4 xq, xk;
+        if (l2) {
+          const float *fq = reinterpret_cast<const float *>(c.smem + oFQ) + r * F32P;
+          const float *fk = reinterpret_cast<const float *>(c.smem + oFK) + r * F32P;
+          xq = l2_back(c.bf(oQ) + r * P128, fq, c.sm().rq[r], pc16);
+          xk = l2_back(c.bf(oK) + r * P128, fk, c.sm().rk[r], pc16);
+        } else {
+          xq = *reinterpret_cast<const uint4 *>(c.bf(oQ) + r * P128 + 8 * pc16);
+          xk = *reinterpret_cast<const uint4 *>(c.bf(oK) + r * P128 + 8 * pc16);
+        }
+        buf_store16(xq, rq, off);
+        buf_store16(xk, rk, off);
       }
     }
     cur = nxt;
@@ -909,7 +999,7 @@ __global__ __launch_bounds__(kThr) void grad_slice_kernel(BwdArgs a) {
 }  // namespace gslice
 
 bool grad_slice_supported(const BwdArgs &a) {
-  return a.p.dtype == 1 && a.p.K == slice::K && a.p.V == slice::V && a.rq == nullptr;
+  return a.p.dtype == 1 && a.p.K == slice::K && a.p.V == slice::V;
 }
 
 hipError_t launch_grad_slice(const BwdArgs &a, hipStream_t st) {

@@ -31,10 +31,6 @@ struct FwdWorkspace {
   size_t hseg = 0;          // fp32 [NS][Hv][K][V]: segment end states (pass 1)
   size_t eseg = 0;          // fp32 [NS][Hv][K][V]: propagated starts (pass 2)
   size_t flags = 0;         // int32 [NS][Hv]: eseg non-zero
-  // with in-library q/k L2 normalisation (l2 set): normalised rows and factors
-  bool l2 = false;
-  size_t qn = 0, kn = 0;    // element type [B*T][Hq][K]
-  size_t rq = 0, rk = 0;    // fp32 [B*T][Hq]: (sum x^2 + eps)^-1/2
   size_t total = 0;
 };
 
@@ -53,6 +49,9 @@ struct Problem {
   int dtype;  // 0 fp32, 1 bf16
   float scale;
   const int32_t *cu;  // device, or null (uniform rows of T tokens)
+  // in-library q/k L2 normalisation: every kernel normalises the q and k
+  // rows it loads (l2n_piece) before they reach LDS
+  int l2;
 };
 
 struct FwdArgs {
@@ -64,6 +63,10 @@ struct FwdArgs {
   float *ht, *g_cum, *A, *h;
   void *h_e;  // per-chunk states in the element type (backward's internal copy)
   void *tm_ext = nullptr;  // per-chunk T there instead of the workspace (state cache)
+  // with l2 and a state cache: prep writes the normalised q, k rows and their
+  // factors here, and the passes after it read those rows
+  void *qn_out = nullptr, *kn_out = nullptr;
+  float *rq_out = nullptr, *rk_out = nullptr;
   char *ws;
   FwdWorkspace wl;
 };
@@ -75,8 +78,8 @@ struct BwdArgs {
   const float *g, *A, *h0, *dht;
   void *dq, *dk, *dv, *dbeta;
   float *dg, *dh0;
-  // set with in-library q/k L2 normalisation (q, k then point at the
-  // normalised rows): per-row factors for the chain rule of dq, dk
+  // set when q, k point at rows the forward normalised (state cache, l2):
+  // their factors, for the chain rule of dq, dk
   const float *rq = nullptr, *rk = nullptr;
   // the forward's state cache ([chunks][Hv][K*V], element type, lane layout), or null:
   // then the states are recomputed into the workspace
@@ -104,8 +107,6 @@ hipError_t launch_rev_slice_main(const BwdArgs &a, hipStream_t stream);
 bool grad_slice_supported(const BwdArgs &a);
 hipError_t launch_grad_slice(const BwdArgs &a, hipStream_t stream);
 // q_hat, k_hat (element type) and their per-row factors from raw q, k
-hipError_t launch_l2norm(const Problem &p, int64_t tokens, const void *q, const void *k,
-                         void *qn, void *kn, float *rq, float *rk, hipStream_t stream);
 
 // Benchmark timing: while enabled on the calling thread, each KernelTimer
 // scope records a HIP event before and after the kernel launched inside it,

@@ -104,7 +104,7 @@ __device__ __forceinline__ void helper_load(HelperRegs<HW> &R, const BwdArgs &a,
 
 template <int HW>
 __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set, float *gates,
-                                              float *scratch, float scale, int lane) {
+                                              float *scratch, float scale, bool l2, int lane) {
   const int h = lane >> 5, r32 = lane & 31, r16 = lane >> 4, pc = lane & 15;
   const float gam = wave_incl_scan(R.g) * kLog2e;
   if (HW != 1) {
@@ -113,8 +113,10 @@ __device__ __forceinline__ void helper_commit(const HelperRegs<HW> &R, bf16 *set
     sg[lane] = gam;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      put_pi(set + oQ + (32 * rbq + 4 * m + r16) * PITCH, pc, R.buf[m]);
-      put_pi(set + oK + (32 * rbk + 4 * m + r16) * PITCH, pc, R.buf[8 + m]);
+      const uint4 xq = l2 ? l2n_piece<bf16, 16>(R.buf[m]) : R.buf[m];
+      const uint4 xk = l2 ? l2n_piece<bf16, 16>(R.buf[8 + m]) : R.buf[8 + m];
+      put_pi(set + oQ + (32 * rbq + 4 * m + r16) * PITCH, pc, xq);
+      put_pi(set + oK + (32 * rbk + 4 * m + r16) * PITCH, pc, xk);
     }
     if (HW != 3) {
 #pragma unroll
@@ -177,7 +179,7 @@ __device__ __forceinline__ void helper_step(HelperRegs<HW> &Rc, HelperRegs<HW> &
   const int cn = c - 1;
   helper_commit<HW>(Rc, reinterpret_cast<bf16 *>(smem + (cn & 1) * SET_BYTES),
                     reinterpret_cast<float *>(smem + 2 * SET_BYTES) + (cn & 1) * GATE_FLOATS,
-                    scratch, a.p.scale, lane);
+                    scratch, a.p.scale, a.p.l2, lane);
   if (HW != 1) helper_load<HW>(Rl, a, it, max(c - 2, c0), lane, 2);
 }
 
@@ -192,7 +194,7 @@ __device__ __forceinline__ void helper_loop(const BwdArgs &a, const Item &it, ch
     helper_load<HW>(R1, a, it, max(cl - 1, c0), lane);
     helper_commit<HW>(R0, reinterpret_cast<bf16 *>(smem + (cl & 1) * SET_BYTES),
                       reinterpret_cast<float *>(smem + 2 * SET_BYTES) + (cl & 1) * GATE_FLOATS,
-                      scratch, a.p.scale, lane);
+                      scratch, a.p.scale, a.p.l2, lane);
   }
   __syncthreads();
   // R1 holds chunk c - 1 at even steps (from c1 - 1), R0 at odd ones

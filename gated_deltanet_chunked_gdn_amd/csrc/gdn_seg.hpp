@@ -151,9 +151,10 @@ struct Pref {
 
 // Load one chunk's q, k, (v-like tile), T, g, beta into registers.
 // vsrc is v (forward) or do (backward); it is skipped when null-like (want_v).
-// Tile bases are computed once per chunk (wave-uniform, scalar registers) and
-// lanes add 32-bit byte offsets, which keeps per-lane 64-bit addresses out of
-// the registers that stay live while the loads are in flight.
+// Every load goes through a buffer whose range ends with the chunk's valid
+// rows (or the tile), so the guards need no branch and nothing waits for a
+// load before its data is committed; the buffer bases are wave-uniform and
+// lanes add 32-bit byte offsets.
 template <typename E, int K, int V, bool WANT_V>
 __device__ __forceinline__ void pref_load(Pref<E, K, V> &pf, const Problem &p, const E *qp,
                                           const E *kp, const E *vsrc, const E *tmat,
@@ -164,51 +165,36 @@ __device__ __forceinline__ void pref_load(Pref<E, K, V> &pf, const Problem &p, c
   const int hq = h / (p.Hv / p.Hq);
   constexpr int PK = K / G::VEC, PVr = V / G::VEC;
   pf.rows = rows;
-  const char *qb = reinterpret_cast<const char *>(qp + (tok0 * p.Hq + hq) * K);
-  const char *kb = reinterpret_cast<const char *>(kp + (tok0 * p.Hq + hq) * K);
   const uint32_t qrs = (uint32_t)(p.Hq * K * sizeof(E));  // bytes between token rows
+  const auto rq = raw_buffer(qp + (tok0 * p.Hq + hq) * K, (uint32_t)rows * qrs);
+  const auto rk = raw_buffer(kp + (tok0 * p.Hq + hq) * K, (uint32_t)rows * qrs);
 #pragma unroll
   for (int m = 0; m < G::NQ; ++m) {
+    // pieces past the tile (idx >= PQ) fall past the range: rows >= 64
     const int idx = tid + kThreads * m;
-    const int r = idx / PK, cv = idx % PK;
-    uint4 zq = make_uint4(0u, 0u, 0u, 0u), zk = zq;
-    if (idx < G::PQ && r < rows) {
-      const uint32_t off = (uint32_t)r * qrs + (uint32_t)cv * 16u;
-      zq = *reinterpret_cast<const uint4 *>(qb + off);
-      zk = *reinterpret_cast<const uint4 *>(kb + off);
-    }
-    pf.q[m] = zq;
-    pf.k[m] = zk;
+    const uint32_t off = (uint32_t)(idx / PK) * qrs + (uint32_t)(idx % PK) * 16u;
+    pf.q[m] = buf_load16(rq, off);
+    pf.k[m] = buf_load16(rk, off);
   }
   if (WANT_V) {
-    const char *vb = reinterpret_cast<const char *>(vsrc + (tok0 * p.Hv + h) * V);
     const uint32_t vrs = (uint32_t)(p.Hv * V * sizeof(E));
+    const auto rv = raw_buffer(vsrc + (tok0 * p.Hv + h) * V, (uint32_t)rows * vrs);
 #pragma unroll
     for (int m = 0; m < G::NV; ++m) {
       const int idx = tid + kThreads * m;
-      const int r = idx / PVr, cv = idx % PVr;
-      uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < G::PV && r < rows)
-        z = *reinterpret_cast<const uint4 *>(vb + (uint32_t)r * vrs + (uint32_t)cv * 16u);
-      pf.v[m] = z;
+      pf.v[m] = buf_load16(rv, (uint32_t)(idx / PVr) * vrs + (uint32_t)(idx % PVr) * 16u);
     }
   }
-  const char *tm = reinterpret_cast<const char *>(tmat + (cgid * p.Hv + h) * 64 * 64);
+  const auto rt = raw_buffer(tmat + (cgid * p.Hv + h) * 64 * 64, (uint32_t)G::PT * 16u);
 #pragma unroll
-  for (int m = 0; m < G::NTM; ++m) {
-    const int idx = tid + kThreads * m;
-    uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    if (idx < G::PT) z = *reinterpret_cast<const uint4 *>(tm + (uint32_t)idx * 16u);
-    pf.t[m] = z;
-  }
-  pf.g = 0.f;
-  pf.b = from_f32<E>(0.f);
-  if (tid < 64 && tid < rows) {
-    const int64_t gi0 = tok0 * p.Hv + h;
-    const uint32_t gi = (uint32_t)tid * (uint32_t)p.Hv;
-    pf.g = g[gi0 + gi];
-    pf.b = beta[gi0 + gi];
-  }
+  for (int m = 0; m < G::NTM; ++m) pf.t[m] = buf_load16(rt, (uint32_t)(tid + kThreads * m) * 16u);
+  // g and beta of row tid (threads 0..63; past the rows and above 63: 0)
+  const int64_t gi0 = tok0 * p.Hv + h;
+  const uint32_t gs = (uint32_t)p.Hv;
+  const uint32_t gn = (uint32_t)rows * gs;
+  pf.g = buf_load_elem<float>(raw_buffer(g + gi0, gn * 4u), (uint32_t)tid * gs * 4u);
+  pf.b = buf_load_elem<E>(raw_buffer(beta + gi0, gn * (uint32_t)sizeof(E)),
+                          (uint32_t)tid * gs * (uint32_t)sizeof(E));
 }
 
 // Per-chunk gate quantities in LDS.

@@ -108,8 +108,12 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_problem_t *p);
  * element type, K * V elements per chunk and v-head, [chunks][Hv] in token
  * order, each state in the library's internal element order) and every
  * chunk's T = (I + A)^-1 (element type, [chunks][Hv][64][64], at the next
- * 256-byte boundary).  With it the backward neither recomputes those states
- * nor rebuilds T, and ignores its A argument. */
+ * 256-byte boundary).  With qk_l2norm it also holds the normalised q and k
+ * rows (element type, [tokens][Hq][K] each) and their factors
+ * (sum x^2 + 1e-6)^-1/2 (fp32, [tokens][Hq] for q, then for k), each piece
+ * at the next 256-byte boundary: the forward normalises every row once and
+ * the backward reads the rows back.  With the cache the backward neither
+ * recomputes those states nor rebuilds T, and ignores its A argument. */
 size_t gdn_state_cache_size(const gdn_problem_t *p);
 
 /* Forward (chunk_gated_delta_rule_fwd of the FlashQLA article, "底层 API").

@@ -78,17 +78,18 @@ def to_dev(p, dev="cuda:0"):
     return out
 
 
-def oracle_fwd(p, unit_mask=None):
+def oracle_fwd(p, unit_mask=None, qk_l2norm=False):
     cu = None if p["cu_seqlens"] is None else p["cu_seqlens"].numpy()
     return token.fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], scale=p["scale"],
-                     initial_state=p["initial_state"], cu_seqlens=cu, unit_mask=unit_mask)
+                     initial_state=p["initial_state"], cu_seqlens=cu, unit_mask=unit_mask,
+                     qk_l2norm=qk_l2norm)
 
 
-def oracle_bwd(p, unit_mask=None):
+def oracle_bwd(p, unit_mask=None, qk_l2norm=False):
     cu = None if p["cu_seqlens"] is None else p["cu_seqlens"].numpy()
     return token.bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], p["do"], p["dht"],
                      scale=p["scale"], initial_state=p["initial_state"], cu_seqlens=cu,
-                     unit_mask=unit_mask)
+                     unit_mask=unit_mask, qk_l2norm=qk_l2norm)
 
 
 def token_mask(p, unit_mask):

@@ -137,7 +137,7 @@ def test_plan_segments_cp_modes():
 
 def test_qk_l2norm_flag():
     base = ws(prob())
-    assert ws(prob(qk_l2norm=1)) > base     # room for the normalised rows
+    assert ws(prob(qk_l2norm=1)) == base    # rows normalised as loaded: no extra room
     assert ws(prob(qk_l2norm=2)) == 0 and fwd_rc(prob(qk_l2norm=2)) == 1
 
 
@@ -148,6 +148,14 @@ def test_state_cache_size():
     assert L.gdn_state_cache_size(ctypes.byref(p)) == 128 * 64 * (128 * 128 + 64 * 64) * 2
     assert L.gdn_state_cache_size(ctypes.byref(prob(T=100))) == 2 * 4 * (128 * 128 + 64 * 64) * 2
     assert L.gdn_state_cache_size(ctypes.byref(prob(Hq=3))) == 0
+    # with qk_l2norm: then the normalised q, k rows ([tokens][Hq][K], bf16)
+    # and their fp32 factors ([tokens][Hq]), each at a 256-byte boundary
+    base = 128 * 64 * (128 * 128 + 64 * 64) * 2
+    rows = 8192 * 32
+    al = lambda x: (x + 255) // 256 * 256
+    want = al(al(al(base) + rows * 128 * 2) + rows * 128 * 2)
+    want = al(want + rows * 4) + rows * 4
+    assert L.gdn_state_cache_size(ctypes.byref(prob(T=8192, Hv=64, Hq=32, qk_l2norm=1))) == want
 
 
 def test_empty_problem_is_valid():

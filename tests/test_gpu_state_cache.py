@@ -34,7 +34,8 @@ def both(gdn, p, cp_mode, l2=False):
     d = to_dev(p)
     kw = dict(scale=d["scale"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
               cp_mode=cp_mode, use_qk_l2norm_in_kernel=l2)
-    cache = gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode)
+    cache = gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode,
+                                  use_qk_l2norm_in_kernel=l2)
     cache.fill_(255)  # NaN in bf16 and fp32: every entry must be written by the forward
     _, A, _, _, _ = gdn.chunk_gated_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                    state_cache=cache, **kw)
@@ -44,7 +45,8 @@ def both(gdn, p, cp_mode, l2=False):
                                                d["do"], dht=d["dht"], **kw)
     # with a cache the backward reads neither A nor anything the forward's
     # intermediates hold: an inference-mode forward plus the cache suffices
-    cache2 = gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode)
+    cache2 = gdn.state_cache_empty(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cp_mode=cp_mode,
+                                   use_qk_l2norm_in_kernel=l2)
     gdn.chunk_gated_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                    return_intermediates=False, state_cache=cache2, **kw)
     no_a = gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None,
@@ -66,9 +68,26 @@ def both(gdn, p, cp_mode, l2=False):
     t_off = (n_st + 255) // 256 * 256
     states = cache[:n_st].view(d["q"].dtype)
     tm = cache[t_off:t_off + nc * Hv * 64 * 64 * es].view(d["q"].dtype)
-    assert cache.numel() == t_off + nc * Hv * 64 * 64 * es
+    end = t_off + nc * Hv * 64 * 64 * es
     assert not torch.isnan(states).any(), "state cache: states left unwritten"
     assert not torch.isnan(tm).any(), "state cache: T left unwritten"
+    if l2:
+        # then the normalised q, k rows and their factors, each at the next
+        # 256-byte boundary: every row of unit norm, every factor 1 / |x|
+        rows = d["q"].shape[0] * d["q"].shape[1] * d["q"].shape[2]
+        al = lambda x: (x + 255) // 256 * 256
+        qn_off = al(end)
+        kn_off = al(qn_off + rows * K * es)
+        rq_off = al(kn_off + rows * K * es)
+        rk_off = al(rq_off + rows * 4)
+        end = rk_off + rows * 4
+        for off, f_off, x in ((qn_off, rq_off, d["q"]), (kn_off, rk_off, d["k"])):
+            xn = cache[off:off + rows * K * es].view(d["q"].dtype).float().view(-1, K)
+            fr = cache[f_off:f_off + rows * 4].view(torch.float32)
+            raw = x.float().reshape(-1, K)
+            assert torch.allclose(xn.norm(dim=1), torch.ones_like(fr), atol=2e-2)
+            assert torch.allclose(fr, torch.rsqrt((raw * raw).sum(1) + 1e-6), rtol=1e-5)
+    assert cache.numel() == end
     return with_cache, recompute
 
 
@@ -104,25 +123,27 @@ def test_cache_matches_recompute_and_oracle(gdn, case):
         # ones from the backward's state pass: two kernels, one recurrence, so
         # the gradients agree to the rounding of the bf16 states
         assert rel(x.float().cpu().numpy(), y.float().cpu().numpy()) <= TOL[dtype], n
-    ref = oracle_bwd(p) if not l2 else None
-    if ref is not None:
-        errs = {n: rel(x, r) for n, x, r in zip(NAMES, got, ref)}
-        bad = {n: e for n, e in errs.items() if not e <= TOL[dtype]}
-        assert not bad, f"{label}: {bad} (all: {errs})"
+    ref = oracle_bwd(p, qk_l2norm=l2)
+    errs = {n: rel(x, r) for n, x, r in zip(NAMES, got, ref)}
+    bad = {n: e for n, e in errs.items() if not e <= TOL[dtype]}
+    assert not bad, f"{label}: {bad} (all: {errs})"
 
 
-def test_full_hv64_t8192_cached_step(gdn):
+@pytest.mark.parametrize("l2", [False, True], ids=["plain", "l2norm"])
+def test_full_hv64_t8192_cached_step(gdn, l2):
     """The benchmark's own step at its full size and in its launch
     configuration: the training forward fills the cache (no A, no g_cum), the
     backward takes it with A = None.  o, the final state and every gradient
     are checked against the oracle on whole q/k groups: v-heads 0, 1 (q/k
-    head 0), 40, 41 (q/k head 20) and 62, 63 (q/k head 31)."""
+    head 0), 40, 41 (q/k head 20) and 62, 63 (q/k head 31).  Also with raw q,
+    k normalised inside the library (the benchmark's --qk-l2norm step)."""
     w = synth.WORKLOADS["hv64_t8192"]
-    p = synth.make(w, with_grads=True)
-    announce("full hv64_t8192 cached fwd+bwd")
+    p = synth.make(w, with_grads=True, normalize_qk=not l2)
+    announce(f"full hv64_t8192 cached fwd+bwd l2={l2}")
     d = to_dev(p)
-    kw = dict(scale=d["scale"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"])
-    cache = gdn.state_cache_empty(d["q"], d["v"])
+    kw = dict(scale=d["scale"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+              use_qk_l2norm_in_kernel=l2)
+    cache = gdn.state_cache_empty(d["q"], d["v"], use_qk_l2norm_in_kernel=l2)
     _, A, o, _, ht = gdn.chunk_gated_delta_rule_fwd(
         d["q"], d["k"], d["v"], d["g"], d["beta"], output_final_state=True,
         return_intermediates=False, return_states=False, state_cache=cache, **kw)
@@ -134,12 +155,12 @@ def test_full_hv64_t8192_cached_step(gdn):
     mask = np.zeros((w.B, w.Hv), dtype=bool)
     mask[:, heads] = True
     tm = token_mask(p, mask)
-    ro, rht = oracle_fwd(p, unit_mask=mask)
+    ro, rht = oracle_fwd(p, unit_mask=mask, qk_l2norm=l2)
     o_np = o.double().cpu().numpy()
     errs = {"o": rel(o_np[tm], ro[tm]),
             "ht": rel(ht.double().cpu().numpy()[mask], rht[mask])}
     blocks = {"o": block_rel_max(o_np, ro, tm)}
-    ref = oracle_bwd(p, unit_mask=mask)
+    ref = oracle_bwd(p, unit_mask=mask, qk_l2norm=l2)
     grp = w.Hv // w.Hq
     qk_heads = sorted({h // grp for h in heads})
     for n, x, r in zip(NAMES, got, ref):
