@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
   extern __shared__ __attribute__((aligned(16))) char smem[];
   E *sK = reinterpret_cast<E *>(smem);
   const Problem &p = a.p;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = wave_of(tid), lane = tid & 63;
   constexpr int nw = kPrepThreads / 64;
   const int G = p.Hv / p.Hq;
   const int lr = lane & 15, lg = lane >> 4;
@@ -151,21 +151,33 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
         locate_chunk(p, reinterpret_cast<const int32_t *>(a.ws + a.wl.chunk_prefix), x.gid);
     x.tok0 = cl.si.tok0 + (int64_t)cl.c * kChunk;
     x.rows = min(kChunk, cl.si.len - cl.c * kChunk);
+    // wave-uniform (scalar registers), so that the buffer descriptors built
+    // on it are scalar too (no per-load loop over distinct descriptors)
+    x.hq = __builtin_amdgcn_readfirstlane(x.hq);
+    x.rows = __builtin_amdgcn_readfirstlane(x.rows);
+    x.gid = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x.gid >> 32)) << 32) |
+                      __builtin_amdgcn_readfirstlane((uint32_t)x.gid));
+    x.tok0 = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x.tok0 >> 32)) << 32) |
+                       __builtin_amdgcn_readfirstlane((uint32_t)x.tok0));
     return x;
   };
-  // raw gate and beta of this wave's next v-head (one v-head ahead; beta
-  // stays in the element type until used, so nothing waits for the load)
-  float gv_n = 0.f;
-  E bv_n = from_f32<E>(0.f);
-  auto load_gb = [&](const Item &x, int hl, bool on) {
+  // raw gate and beta of a v-head of an item (beta stays in the element
+  // type until used, so nothing waits for the load); the loads are
+  // unconditional, with on = false their range is empty
+  auto load_gb = [&](float &gv, E &bv, const Item &x, int hl, bool on) {
     const int64_t g0 = x.tok0 * p.Hv + x.hq * G + hl;
     const uint32_t rs = (uint32_t)p.Hv;
     const uint32_t n = on && hl < G ? (uint32_t)x.rows * rs : 0u;
     const auto rg = raw_buffer(a.g + g0, n * 4u);
     const auto rb = raw_buffer(reinterpret_cast<const E *>(a.beta) + g0, n * (uint32_t)sizeof(E));
-    gv_n = buf_load_elem<float>(rg, (uint32_t)lane * rs * 4u);
-    bv_n = buf_load_elem<E>(rb, (uint32_t)lane * rs * (uint32_t)sizeof(E));
+    gv = buf_load_elem<float>(rg, (uint32_t)lane * rs * 4u);
+    bv = buf_load_elem<E>(rb, (uint32_t)lane * rs * (uint32_t)sizeof(E));
   };
+  // this wave's first v-head of the current item (loaded with its k tile, a
+  // whole item ahead) and of the next one; the wave's later v-heads of an
+  // item (more than two v-heads per q/k head) one v-head ahead
+  float gv_f = 0.f, gv_x = 0.f, gv_n = 0.f;
+  E bv_f = from_f32<E>(0.f), bv_x = bv_f, bv_n = bv_f;
   const E *kp = reinterpret_cast<const E *>(a.k);
   const E *qp = reinterpret_cast<const E *>(a.q);
   constexpr int VEC = 16 / (int)sizeof(E);
@@ -190,12 +202,12 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
   };
   if (blockIdx.x >= n_items) return;
   Item cur = item_of(blockIdx.x);
-  load_gb(cur, w, true);
+  load_gb(gv_f, bv_f, cur, w, true);
   load_k(cur, true);
   E *tmat = reinterpret_cast<E *>(a.tm_ext ? a.tm_ext : a.ws + a.wl.tmat);
   constexpr int LD = 17, BS = C::BS;
   float *W = reinterpret_cast<float *>(smem) + w * C::floatsW;
-  float *sA = W + C::fA, *sT = W + C::fT, *sAd = W + C::fAd, *sM = W + C::fM;
+  float *sA = W + C::fA, *sT = W + C::fT, *sAd = W + C::fAd;
   // lower block (i >= j) of T (diagonal blocks first), off-diagonal block
   // (i > j) of A
 #define TB(i, j) (sT + ((i) == (j) ? (i) : 4 + ((i) * ((i) - 1)) / 2 + (j)) * BS)
@@ -266,20 +278,13 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
     __syncthreads();  // the per-wave buffers alias sK
     const Item nxt = has_next ? item_of(it_next) : cur;
     load_k(nxt, has_next);
+    load_gb(gv_x, bv_x, nxt, w, has_next);
     for (int hl = w; hl < G; hl += nw) {
       const int h = hq * G + hl;
       const int64_t gi = (tok0 + lane) * p.Hv + h;
-      const float gv = gv_n, bv = to_f32(bv_n);
-      {
-        // this wave's next v-head: in this item, else the next item's first
-        const bool in_item = hl + nw < G;
-        Item x;
-        x.hq = in_item ? cur.hq : nxt.hq;
-        x.rows = in_item ? cur.rows : nxt.rows;
-        x.gid = in_item ? cur.gid : nxt.gid;
-        x.tok0 = in_item ? cur.tok0 : nxt.tok0;
-        load_gb(x, in_item ? hl + nw : w, in_item || has_next);
-      }
+      const bool first = hl == w;
+      const float gv = first ? gv_f : gv_n, bv = to_f32(first ? bv_f : bv_n);
+      if (hl + nw < G) load_gb(gv_n, bv_n, cur, hl + nw, true);
       const float gam = wave_incl_scan(gv);
       float *sG = W + C::fG, *sB = W + C::fB;
       sG[lane] = gam * kLog2e;
@@ -334,27 +339,38 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
         for (int r = 0; r < 16; ++r) tb[r * LD + c] = x[r];
       }
       wave_sync();
-      // level 1: T_{b+1,b} = -T_{b+1,b+1} A_{b+1,b} T_bb
+      // level 1: T_{b+1,b} = -T_{b+1,b+1} A_{b+1,b} T_bb, the three blocks
+      // side by side (each inner product waits in T_{b+1,b}'s own place)
+      {
+        f32x4 m[3];
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        f32x4 m = mm16(zero4(), AB(b + 1, b), TB(b, b), LD);
-        put16(sM, LD, m, 1.f);
+        for (int b = 0; b < 3; ++b) m[b] = mm16(zero4(), AB(b + 1, b), TB(b, b), LD);
+#pragma unroll
+        for (int b = 0; b < 3; ++b) put16(TB(b + 1, b), LD, m[b], 1.f);
         wave_sync();
-        f32x4 t1 = mm16(zero4(), TB(b + 1, b + 1), sM, LD);
+#pragma unroll
+        for (int b = 0; b < 3; ++b) m[b] = mm16(zero4(), TB(b + 1, b + 1), TB(b + 1, b), LD);
         wave_sync();
-        put16(TB(b + 1, b), LD, t1, -1.f);
+#pragma unroll
+        for (int b = 0; b < 3; ++b) put16(TB(b + 1, b), LD, m[b], -1.f);
       }
       wave_sync();
       // level 2: T_{b+2,b} = -T_{b+2,b+2} (A_{b+2,b} T_bb + A_{b+2,b+1} T_{b+1,b})
+      {
+        f32x4 m[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        f32x4 m = mm16(zero4(), AB(b + 2, b), TB(b, b), LD);
-        m = mm16(m, AB(b + 2, b + 1), TB(b + 1, b), LD);
-        put16(sM, LD, m, 1.f);
+        for (int b = 0; b < 2; ++b) {
+          m[b] = mm16(zero4(), AB(b + 2, b), TB(b, b), LD);
+          m[b] = mm16(m[b], AB(b + 2, b + 1), TB(b + 1, b), LD);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) put16(TB(b + 2, b), LD, m[b], 1.f);
         wave_sync();
-        f32x4 t2 = mm16(zero4(), TB(b + 2, b + 2), sM, LD);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) m[b] = mm16(zero4(), TB(b + 2, b + 2), TB(b + 2, b), LD);
         wave_sync();
-        put16(TB(b + 2, b), LD, t2, -1.f);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) put16(TB(b + 2, b), LD, m[b], -1.f);
       }
       wave_sync();
       // level 3: T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
@@ -362,10 +378,11 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
         f32x4 m = mm16(zero4(), AB(3, 0), TB(0, 0), LD);
         m = mm16(m, AB(3, 1), TB(1, 0), LD);
         m = mm16(m, AB(3, 2), TB(2, 0), LD);
-        put16(sM, LD, m, 1.f);
+        put16(TB(3, 0), LD, m, 1.f);
         wave_sync();
-        f32x4 t3 = mm16(zero4(), TB(3, 3), sM, LD);
-        put16(TB(3, 0), LD, t3, -1.f);
+        m = mm16(zero4(), TB(3, 3), TB(3, 0), LD);
+        wave_sync();
+        put16(TB(3, 0), LD, m, -1.f);
       }
       wave_sync();
       // T out (element type, chunk-contiguous rows), 16 bytes a lane, in two
@@ -421,6 +438,8 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
     }
     __syncthreads();  // the per-wave buffers are read out before the next k tile lands
     cur = nxt;
+    gv_f = gv_x;
+    bv_f = bv_x;
   }
 #undef TB
 #undef AB

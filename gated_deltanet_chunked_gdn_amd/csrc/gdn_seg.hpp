@@ -162,6 +162,14 @@ __device__ __forceinline__ void pref_load(Pref<E, K, V> &pf, const Problem &p, c
                                           int rows, int h, int64_t cgid,
                                           int tid = threadIdx.x) {
   using G = Geo<E, K, V>;
+  // the chunk's coordinates are the same for every lane: as scalars, the
+  // buffer descriptors built on them are scalar (no per-load descriptor loop)
+  tok0 = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tok0 >> 32)) << 32) |
+                   __builtin_amdgcn_readfirstlane((uint32_t)tok0));
+  cgid = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)cgid >> 32)) << 32) |
+                   __builtin_amdgcn_readfirstlane((uint32_t)cgid));
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  h = __builtin_amdgcn_readfirstlane(h);
   const int hq = h / (p.Hv / p.Hq);
   constexpr int PK = K / G::VEC, PVr = V / G::VEC;
   pf.rows = rows;
@@ -300,7 +308,9 @@ __device__ __forceinline__ void tiles_old_t(TilesOld<E, K, V> &o, const E *dstT,
   using G = Geo<E, K, V>;
   const int w = wave_of(tid), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  if (!G::owns(w)) return;
+  // (no branch where every wave owns tiles: loads under a branch are waited
+  // for where it joins)
+  if (G::NT < kNW * G::NTS && !G::owns(w)) return;
   const int rt = G::srt(w);
 #pragma unroll
   for (int m = 0; m < G::NTS; ++m) {
@@ -376,7 +386,9 @@ __device__ __forceinline__ void tiles_old_l(TilesOld<E, K, V> &o, const E *dst,
   using G = Geo<E, K, V>;
   const int w = wave_of(tid), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  if (!G::owns(w)) return;
+  // (no branch where every wave owns tiles: loads under a branch are waited
+  // for where it joins)
+  if (G::NT < kNW * G::NTS && !G::owns(w)) return;
   const int rt = G::srt(w);
 #pragma unroll
   for (int m = 0; m < G::NTS; ++m) {
