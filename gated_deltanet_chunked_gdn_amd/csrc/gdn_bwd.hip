@@ -146,6 +146,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
 
   if (c_begin >= c_end)
     return MODE == kRFix ? !block_any(tiles_significant<E, K, V>(st), S.flag) : false;
+  const float thr = MODE == kRFix ? fix_threshold<E, K, V>(st, S.flag) : 0.f;
   Pref<E, K, V> pf;
   {
     const int c = c_end - 1;
@@ -308,7 +309,7 @@ __device__ __forceinline__ bool rev_run(const BwdArgs &a, const RSmem &S,
     }
     tiles_to_lds_t<E, K, V>(st, sDt, tid);
     if (MODE == kRFix) {
-      zero_exit = !block_any(tiles_significant<E, K, V>(st), S.flag);
+      zero_exit = !block_any(tiles_significant<E, K, V>(st, thr), S.flag);
     } else {
       __syncthreads();
     }

@@ -582,6 +582,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
 
   if (c_begin >= c_end)
     return MODE == kFix ? !block_any(tiles_significant<E, K, V>(st), S.flag) : false;
+  const float thr = MODE == kFix ? fix_threshold<E, K, V>(st, S.flag) : 0.f;
   Pref<E, K, V> pf;
   {
     const int rows = min(kChunk, si.len - c_begin * kChunk);
@@ -811,7 +812,7 @@ __device__ __forceinline__ bool run_chunks(const FwdArgs &a, const Smem &S,
     }
     tiles_to_lds_t<E, K, V>(st, sSt, tid);
     if (MODE == kFix) {
-      zero_exit = !block_any(tiles_significant<E, K, V>(st), S.flag);
+      zero_exit = !block_any(tiles_significant<E, K, V>(st, thr), S.flag);
     } else {
       __syncthreads();
     }

@@ -498,18 +498,43 @@ __device__ __forceinline__ void tiles_to_lds_t(const Tiles<Geo<E, K, V>::NTS> &s
 }
 
 // True when some element of the (correction) state has magnitude at least
-// 2^-126, the smallest normal fp32.  The fix-up passes stop once it fails:
-// what they drop is a state whose every element is zero or denormal, so its
-// further contributions are of order 2^-126 (the decay drives a correction
-// through the denormal range in about one more chunk).
+// thr (by default 2^-126, the smallest normal fp32).  The fix-up passes stop
+// once it fails for fix_threshold(): what they drop is a correction below
+// 2^-30 of the one they started with (or zero / denormal), whose further
+// contributions to outputs and states lie below the fp32 resolution of the
+// contributions already made.
 template <typename E, int K, int V>
-__device__ __forceinline__ bool tiles_significant(const Tiles<Geo<E, K, V>::NTS> &s) {
+__device__ __forceinline__ bool tiles_significant(const Tiles<Geo<E, K, V>::NTS> &s,
+                                                  float thr = 0x1p-126f) {
   bool nz = false;
 #pragma unroll
   for (int m = 0; m < Geo<E, K, V>::NTS; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nz |= (__builtin_fabsf(s[m][i]) >= 0x1p-126f);
+    for (int i = 0; i < 4; ++i) nz |= (__builtin_fabsf(s[m][i]) >= thr);
   return nz;
+}
+
+// Exit threshold of a fix-up pass whose correction starts as s: 2^-30 of its
+// largest magnitude over the workgroup, at least 2^-126 (uses 8 ints of LDS;
+// every thread of the workgroup calls it).
+template <typename E, int K, int V>
+__device__ __forceinline__ float fix_threshold(const Tiles<Geo<E, K, V>::NTS> &s, int *sflag) {
+  float x = 0.f;
+#pragma unroll
+  for (int m = 0; m < Geo<E, K, V>::NTS; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x = __builtin_fmaxf(x, __builtin_fabsf(s[m][i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, o, 64));
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) sflag[w] = __builtin_bit_cast(int, x);
+  __syncthreads();
+  int r = 0;  // non-negative floats order as their bit patterns
+#pragma unroll
+  for (int i = 0; i < kNW; ++i) r = max(r, sflag[i]);
+  __syncthreads();
+  return __builtin_fmaxf(0x1p-126f, 0x1p-30f * __builtin_bit_cast(float, r));
 }
 
 // Workgroup-wide OR of a per-thread flag (uses 8 ints of LDS).
