@@ -109,6 +109,19 @@ CASES = [
     ("bf16 l2norm cp=1", lambda: synth.custom(1, 260, 2, 4, 128, 128, dtype="bf16", seed=10,
                                               gate="slow", h0=True, grads=True,
                                               normalize_qk=False), "bf16", 1, True),
+    ("bf16 l2norm varlen+empty cp=2", lambda: synth.custom(1, 0, 2, 4, 128, 128, dtype="bf16",
+                                                           seed=11, gate="default",
+                                                           lengths=[0, 1, 64, 330, 0, 700, 63],
+                                                           h0=True, grads=True,
+                                                           normalize_qk=False), "bf16", 2, True),
+    ("bf16 l2norm 3 v-heads per q/k head", lambda: synth.custom(1, 200, 1, 3, 128, 128,
+                                                                dtype="bf16", seed=12,
+                                                                gate="slow", h0=True, grads=True,
+                                                                normalize_qk=False),
+     "bf16", -1, True),
+    ("f32 l2norm cp=1", lambda: synth.custom(1, 200, 1, 2, 64, 64, dtype="f32", seed=13,
+                                             gate="slow", h0=True, grads=True,
+                                             normalize_qk=False), "f32", 1, True),
 ]
 
 
