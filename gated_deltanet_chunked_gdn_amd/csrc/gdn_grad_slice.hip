@@ -542,7 +542,10 @@ __device__ __forceinline__ void e_tiles_out(const f32x16 (&eacc)[2], const f32x1
 // writes dx.
 constexpr int F32P = 132;
 constexpr int oFQ = oS, oFK = oO;
-static_assert(64 * F32P * 4 <= oO - oS && 64 * F32P * 4 <= oPEt - oO, "fp32 staging");
+// (dk reaches into P^T's first rows, which the next item rewrites whole; it
+// stays clear of P^T's zero block, rows 32..63 of positions 0..31)
+static_assert(oFQ + 64 * F32P * 4 <= oO && oFK + 64 * F32P * 4 <= oPt + 32 * P64 * 2,
+              "fp32 staging");
 __device__ __forceinline__ void stage_f32(const f32x16 (&x)[2], int off, int rt, int kp,
                                           const Ctx &c) {
   float *f = reinterpret_cast<float *>(c.smem + off);
