@@ -331,6 +331,41 @@ def config_entries(gdn, synth, torch, dev, args, cold_buf):
     out["bwd_b2_t16384_hv16"] = ent
     del d, p, A, cache
     torch.cuda.empty_cache()
+    # the pages' benchmark axis: head counts 48 .. 8 (TP2 .. TP8 of the
+    # headline's 64; H_q = H_v / 2, T = 8192), the inference forward and the
+    # cached training step (fwd + bwd) at each
+    sw = {}
+    for hv in synth.SWEEP_HV:
+        if hv == 64:
+            continue  # the headline line itself
+        w = synth.sweep_workload(hv)
+        p = synth.make(w)
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+        nch = nchunks_of(w, p)
+        ntok = w.B * w.T
+        kw = dict(scale=d["scale"], initial_state=d["initial_state"])
+
+        def f():
+            gdn.chunk_gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                       output_final_state=True, **kw)
+        fe = timing(torch, f, args.reps, cold_buf, ntok, fpc * nch * w.Hv, PEAK_BF16)
+        cache = gdn.state_cache_empty(d["q"], d["v"])
+
+        def step():
+            gdn.chunk_gated_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                           output_final_state=True, return_intermediates=False,
+                                           return_states=False, state_cache=cache, **kw)
+            gdn.chunk_gated_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None,
+                                           d["do"], dht=d["dht"], state_cache=cache, **kw)
+        se = timing(torch, step, args.reps, cold_buf, ntok, (fpc + bpc) * nch * w.Hv, PEAK_BF16)
+        sw[str(hv)] = {"H_q": w.Hq, "T": w.T,
+                       "segments": gdn.plan_segments(d["q"], d["k"], d["v"]),
+                       "fwd_ms": fe["ms"], "fwd_pct_mfma_peak": round(fe["pct_mfma_peak"], 2),
+                       "step_ms": se["ms"], "step_tokens_per_s": se["tokens_per_s"],
+                       "step_pct_mfma_peak": round(se["pct_mfma_peak"], 2)}
+        del d, p, cache
+        torch.cuda.empty_cache()
+    out["head_sweep_t8192"] = sw
     return out
 
 
