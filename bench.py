@@ -398,7 +398,7 @@ def main():
                          "segment length; prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path; "
+        print("bench.py measures one GPU: the library has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
