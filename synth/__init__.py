@@ -18,7 +18,7 @@ draws float32 standard normal, in this order):
 then q, k, v, beta, do are cast to the working dtype (bf16 rounding is
 round-to-nearest-even, done by torch).  scale = K^-0.5.
 
-Gate variants (same seed): "slow" divides g by 100, "nodecay" sets g = 0.
+Gate variants (same seed): "slow" divides g by 100, "moderate" by 10, "nodecay" sets g = 0.
 These expose the carried state, which the default gates (about e^-52 per
 64-token chunk) make numerically invisible after a chunk or two.
 """
@@ -122,6 +122,8 @@ def make(w: Workload, gate: str = "default", T: Optional[int] = None,
     beta = (1.0 / (1.0 + np.exp(-sn(B, Ttot, Hv)))).astype(np.float32)
     if gate == "slow":
         g = (g / np.float32(100.0)).astype(np.float32)
+    elif gate == "moderate":
+        g = (g / np.float32(10.0)).astype(np.float32)
     elif gate == "nodecay":
         g = np.zeros_like(g)
     elif gate != "default":

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_util import (BLOCK_TOL, TOL, announce, block_rel_max, oracle_fwd, rel,
+from tests.gpu_util import (BLOCK_TOL, TOL, announce, block_rel_max, oracle_bwd, oracle_fwd, rel,
                             to_dev, token_mask)
 
 pytestmark = pytest.mark.gpu
@@ -58,6 +58,25 @@ def test_tiny_f32_workload(gdn):
 def test_tiny_f32_gates_and_cp(gdn, gate, cp):
     p = synth.make(synth.WORKLOADS["tiny_f32"], gate=gate, with_h0=True)
     check(gdn, p, "f32", cp_mode=cp, label=f"tiny_f32 {gate}")
+
+
+def test_fixup_stops_on_relative_decay(gdn):
+    """Gates that decay by about e^-5 a chunk: the correction pass crosses the
+    2^-30 relative stop a few chunks into each 8-chunk segment, so every
+    segment after the first exits early; fp32 at its 1e-5 bound against the
+    oracle, forward and backward."""
+    p = synth.custom(1, 2048, 1, 2, 32, 32, dtype="f32", seed=21, gate="moderate", h0=True,
+                     grads=True)
+    check(gdn, p, "f32", cp_mode=8, label="moderate gates, 8-chunk segments")
+    d = to_dev(p)
+    got = gdn.chunk_gated_delta_rule_bwd(
+        d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["do"], dht=d["dht"],
+        scale=d["scale"], initial_state=d["initial_state"], cp_mode=8)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(p)
+    errs = {n: rel(x, r) for n, x, r in zip(["dq", "dk", "dv", "db", "dg", "dh0"], got, ref)}
+    bad = {n: e for n, e in errs.items() if not e <= TOL["f32"]}
+    assert not bad, f"{bad} (all {errs})"
 
 
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 257])
